@@ -1,0 +1,214 @@
+/*
+ * moe.h -- C ABI of the routed sparse-MoE layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (reference page "Agent Field Notes -- full corpus"):
+ *   router logits -> float32 softmax with normalized top-k selection
+ *     (AFN-001 "Porting Qwen3.8-Flash-Next to Hebrus: evidence before
+ *     execution", section "Phase 1: separate math from acceleration");
+ *   exact expert IDs in rank order (AFN-021 "Replay decode as prefill ...",
+ *     section "The key equivalence -- and where it breaks"), equal scores
+ *     resolved toward the lower index while choosing membership (AFN-017
+ *     "Top-k chooses the set; time chooses the order", section "Tie handling
+ *     belongs to membership");
+ *   token rows grouped by expert so every selected expert record is read once
+ *     per batch (AFN-019 "Hide SSD misses before the router knows they
+ *     exist", sections "Why overlap alone cannot defeat the byte roofline"
+ *     and "Hypothesis H5");
+ *   SwiGLU experts: gate and up together, down after the intermediate exists,
+ *     results in separate slots, weighted sum in route-rank order (AFN-019,
+ *     section "Hypothesis H4: ExpertMajor should stream as a wavefront, not a
+ *     barrier"); geometry and parameter count per expert (gate [I x H] + up
+ *     [I x H] + down [H x I]) from AFN-019 "Why overlap alone cannot defeat
+ *     the byte roofline".
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory)
+ *   owned by the caller; the library never allocates device memory and keeps
+ *   no state between calls.  Scratch memory is the caller's workspace of at
+ *   least moe_workspace_size(shape) bytes (NULL allowed when that is 0).
+ * - Every call only ENQUEUES work on `stream` (NULL = the null stream) and
+ *   returns without synchronizing.  Calls on different streams with disjoint
+ *   outputs and workspaces are independent.
+ * - Row-major, densely packed layouts; every pointer 16-byte aligned.
+ * - Validation is complete before anything is enqueued: a non-MOE_OK return
+ *   means no kernel was launched and no output byte was written
+ *   (fail-closed, the rule of AFN-001 section "Phase 3: reject before the
+ *   GPU exists").  MOE_E_DEVICE reports a HIP launch error; device faults
+ *   surface at the caller's next synchronization.
+ * - Index tensors are int32; weights and logits are float32.
+ *
+ * Domain (MOE_E_SHAPE / MOE_E_LIMIT otherwise):
+ *   0 <= T <= 131072 (T == 0 is a no-op returning MOE_OK),
+ *   1 <= top_k <= E <= 1024,
+ *   H > 0 with H % 128 == 0, I > 0 with I % 32 == 0, H, I <= 65536,
+ *   T * top_k < 2^31 and T * max(E, H) < 2^31.
+ * Formats (MOE_E_DTYPE / MOE_E_FORMAT otherwise):
+ *   act MOE_DT_F32  with wfmt MOE_WF_DENSE (float32 weights);
+ *   act MOE_DT_BF16 with wfmt MOE_WF_DENSE (bf16 weights), MOE_WF_INT4_G32
+ *   or MOE_WF_INT2_G32 (the router weight is always in the act type).
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_NULL = 1,       /* a required pointer is NULL                          */
+  MOE_E_SHAPE = 2,      /* a dimension is outside the domain above             */
+  MOE_E_DTYPE = 3,      /* unknown activation type                            */
+  MOE_E_FORMAT = 4,     /* unknown weight format or unsupported combination    */
+  MOE_E_ALIGN = 5,      /* a pointer is not 16-byte aligned                    */
+  MOE_E_ALIAS = 6,      /* an output overlaps an input or another output       */
+  MOE_E_WORKSPACE = 7,  /* workspace NULL or smaller than moe_workspace_size() */
+  MOE_E_LIMIT = 8,      /* index arithmetic would exceed 2^31                  */
+  MOE_E_DEVICE = 9,     /* HIP reported an error while enqueuing               */
+  MOE_E_FLAGS = 10      /* unknown bit in moe_shape.flags                      */
+} moe_status;
+
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
+
+/* Expert weight storage.  Low-bit formats (AFN-019, "Why overlap alone cannot
+ * defeat the byte roofline": low-bit storage) hold signed two's-complement
+ * codes q with one IEEE fp16 scale s per 32 consecutive elements along the
+ * reduction axis; the weight is q * s.  Codes are packed little-endian along
+ * the reduction axis: element k of a row is in byte k/2, low nibble first
+ * (int4), or in byte k/4 at bit 2*(k%4) (int2). */
+typedef enum { MOE_WF_DENSE = 0, MOE_WF_INT4_G32 = 1, MOE_WF_INT2_G32 = 2 } moe_wformat;
+
+typedef struct {
+  int32_t T;       /* tokens in the batch                        */
+  int32_t H;       /* hidden width                               */
+  int32_t E;       /* routed experts                             */
+  int32_t I;       /* expert intermediate width                  */
+  int32_t top_k;   /* experts selected per token                 */
+  int32_t act;     /* moe_dtype of x, W_router, dense W, Y, out   */
+  int32_t wfmt;    /* moe_wformat of the expert weights          */
+  uint32_t flags;  /* reserved: must be 0                        */
+} moe_shape;
+
+/* Expert weights, expert-major (one contiguous record per component).
+ *   dense: gate, up [E][I][H], down [E][H][I] in the act type.
+ *   int4 : gate, up uint8 [E][I][H/2], down uint8 [E][H][I/2];
+ *   int2 : gate, up uint8 [E][I][H/4], down uint8 [E][H][I/4];
+ *   scales (low-bit only, fp16 bit patterns): gate_scale, up_scale
+ *   [E][I][H/32], down_scale [E][H][I/32]; must be NULL for dense. */
+typedef struct {
+  const void* gate;
+  const void* up;
+  const void* down;
+  const uint16_t* gate_scale;
+  const uint16_t* up_scale;
+  const uint16_t* down_scale;
+} moe_experts;
+
+/* Per-expert permutation of the P = T*top_k (token, slot) pairs, pair index
+ * p = t*top_k + j.  Rows of expert e are rows offsets[e] .. offsets[e+1]-1,
+ * in ascending p (hence ascending token).  All arrays int32, device memory:
+ *   counts[E], offsets[E+1], sorted_pair[P] (row -> p), pair_row[P]
+ *   (p -> row), active[E] (the first *n_active entries are the experts with
+ *   counts > 0 in ascending order; the rest are -1), n_active[1]. */
+typedef struct {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pair;
+  int32_t* pair_row;
+  int32_t* active;
+  int32_t* n_active;
+} moe_perm;
+
+/* Bytes of workspace every entry point below needs for this shape (the
+ * maximum over all of them, so one buffer serves every call).  Host-only,
+ * pure.  Returns 0 for an invalid shape. */
+size_t moe_workspace_size(const moe_shape* shape);
+
+/* Static description of a status code; never NULL. */
+const char* moe_status_str(int status);
+
+/* Router: logits[t][e] = sum_h x[t][h] * w_router[e][h] + bias[e], then the
+ * top_k experts of each token by (logit descending, expert index ascending),
+ * emitted in rank order, and their weights w[t][j] = exp(l_j - l_0) /
+ * sum_i exp(l_i - l_0) over the selected logits (equal to the full float32
+ * softmax renormalized over the selection).
+ *   x [T][H] act; w_router [E][H] act; router_bias float [E] or NULL;
+ *   topk_ids int32 [T][top_k], topk_w float [T][top_k] (outputs);
+ *   logits float [T][E] or NULL (optional output, the float32 logits the
+ *   selection used).
+ * bf16: the exact bf16 products are summed in float32 within each 32-wide
+ * chunk of H and the chunk sums in float64, then rounded once to float32.
+ * float32: products and sums in float64, rounded once to float32. */
+int moe_route(const moe_shape* shape, const void* x, const void* w_router,
+              const float* router_bias, int32_t* topk_ids, float* topk_w,
+              float* logits, void* workspace, size_t workspace_bytes,
+              hipStream_t stream);
+
+/* Stable grouping of the pairs by expert (the permutation described at
+ * moe_perm).  Also writes the grouped-FFN tile plan into the workspace (read
+ * by moe_ffn_gate_up and moe_ffn_down).  topk_ids [T][top_k]: every entry in [0, E) and the top_k
+ * entries of one token distinct (as moe_route produces); other inputs are
+ * memory-safe but give an unspecified permutation. */
+int moe_permute(const moe_shape* shape, const int32_t* topk_ids,
+                const moe_perm* perm, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/* Grouped SwiGLU experts.  For every row r of expert e with pair p =
+ * sorted_pair[r] and token t = p / top_k:
+ *   y[r][n] = sum_i W_down[e][n][i] * silu(g_i) * u_i,
+ *   g_i = sum_h W_gate[e][i][h] x[t][h],  u_i = sum_h W_up[e][i][h] x[t][h].
+ * Each active expert's weights are streamed from memory once per call for
+ * its whole row set when it has at most 64 rows (otherwise once per 64-row
+ * tile).  perm: counts, offsets, sorted_pair, active, n_active are read
+ * (pair_row is not used).  y [P][H] act (output, rows in permuted order).
+ * The SwiGLU intermediate is kept in the act type (bf16 or float32). */
+int moe_grouped_ffn(const moe_shape* shape, const void* x,
+                    const moe_experts* experts, const moe_perm* perm, void* y,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The two components of moe_grouped_ffn as separate calls, for callers
+ * that schedule them separately (AFN-019, "Hypothesis H4": gate and up are
+ * used together, down only after the SwiGLU intermediate exists):
+ *   moe_ffn_gate_up: h[r][i] = silu(g_i) * u_i for every row r (h [P][I] in
+ *     the act type, output; rows in permuted order);
+ *   moe_ffn_down:    y[r][n] = sum_i W_down[e][n][i] * h[r][i].
+ * Both read the FFN tile plan that moe_permute (or moe_layer) leaves in the
+ * workspace for this shape: call moe_permute with the same shape and
+ * workspace first and do not write the workspace in between.  perm supplies
+ * sorted_pair (gate/up only).  Each call is one kernel launch. */
+int moe_ffn_gate_up(const moe_shape* shape, const void* x,
+                    const moe_experts* experts, const moe_perm* perm, void* h,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+int moe_ffn_down(const moe_shape* shape, const void* h,
+                 const moe_experts* experts, void* y, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/* Route-rank-order combine: out[t][n] = residual[t][n] +
+ * sum_{j=0}^{top_k-1} topk_w[t][j] * y[pair_row[t*top_k+j]][n], accumulated
+ * in float32 with j ascending, rounded once to the act type.
+ *   y [P][H] act; pair_row [P]; topk_w [T][top_k]; residual [T][H] act or
+ *   NULL; out [T][H] act (must not overlap y, residual or topk_w). */
+int moe_combine(const moe_shape* shape, const void* y, const int32_t* pair_row,
+                const float* topk_w, const void* residual, void* out,
+                hipStream_t stream);
+
+/* The whole layer: moe_route -> moe_permute -> moe_grouped_ffn ->
+ * moe_combine with the same semantics, enqueued back to back.  perm may be
+ * NULL (the permutation then lives in the workspace); residual may be NULL;
+ * topk_ids/topk_w are outputs.  out must not overlap x or residual. */
+int moe_layer(const moe_shape* shape, const void* x, const void* w_router,
+              const float* router_bias, const moe_experts* experts,
+              const void* residual, void* out, int32_t* topk_ids, float* topk_w,
+              const moe_perm* perm, void* workspace, size_t workspace_bytes,
+              hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

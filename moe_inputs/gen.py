@@ -10,8 +10,8 @@ bytes that were actually generated):
 * normals are drawn in float32, scaled by the stated standard deviation and
   rounded once (round-to-nearest-even) to the storage type; the rounded values
   are the inputs;
-* expert weights are drawn one expert at a time, in expert order, from the
-  (tensor, layer) stream;
+* expert weights are drawn in blocks of up to 32 experts, in expert order,
+  from the (tensor, layer) stream;
 * low-bit experts: signed symmetric codes, qmax = 2**(b-1) - 1 (int4 -> +-7,
   int2 -> +-1), one fp16 scale per 32 consecutive elements of the reduction
   axis, s = fp16(max|w| / qmax), q = clamp(round_half_even(w / s), +-qmax)
@@ -37,6 +37,7 @@ from .configs import MoEConfig
 _ACT_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 _BITS = {"int4_g32": 4, "int2_g32": 2}
 GROUP = 32
+EXPERT_BLOCK = 32
 
 
 def _generator(cfg: MoEConfig, tensor: str, layer: int, batch: int, device) -> torch.Generator:
@@ -109,17 +110,19 @@ def make_experts(cfg: MoEConfig, layer: int = 0, device="cpu", n_experts: Option
     for name, (rows, K) in (("gate", (cfg.I, cfg.H)), ("up", (cfg.I, cfg.H)),
                             ("down", (cfg.H, cfg.I))):
         g = _generator(cfg, name, layer, 0, device)
+        blocks = [(e0, min(E, e0 + EXPERT_BLOCK)) for e0 in range(0, E, EXPERT_BLOCK)]
         if cfg.wfmt == "dense":
             t = torch.empty((E, rows, K), dtype=_ACT_DTYPE[cfg.act], device=device)
-            for e in range(E):
-                t[e] = _normal((rows, K), cfg.expert_std, g, device).to(t.dtype)
+            for e0, e1 in blocks:
+                t[e0:e1] = _normal((e1 - e0, rows, K), cfg.expert_std, g, device).to(t.dtype)
             out[name], out[name + "_scale"] = t, None
         else:
             bits = _BITS[cfg.wfmt]
             pk = torch.empty((E, rows, K * bits // 8), dtype=torch.uint8, device=device)
             sc = torch.empty((E, rows, K // GROUP), dtype=torch.float16, device=device)
-            for e in range(E):
-                pk[e], sc[e] = quantize_pack(_normal((rows, K), cfg.expert_std, g, device), bits)
+            for e0, e1 in blocks:
+                pk[e0:e1], sc[e0:e1] = quantize_pack(
+                    _normal((e1 - e0, rows, K), cfg.expert_std, g, device), bits)
             out[name], out[name + "_scale"] = pk, sc
     return out
 

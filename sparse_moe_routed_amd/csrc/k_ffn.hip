@@ -1,0 +1,381 @@
+// Grouped SwiGLU experts: gate+up with the SwiGLU epilogue, then down.
+//
+// Reference: "Agent Field Notes -- full corpus", AFN-019 "Hide SSD misses
+// before the router knows they exist":
+//   section "Hypothesis H4: ExpertMajor should stream as a wavefront, not a
+//   barrier" -- gate and up are consumed together, down only after the SwiGLU
+//   intermediate exists, and every (token, expert) result goes to its own slot;
+//   section "Why overlap alone cannot defeat the byte roofline" -- one expert
+//   is gate [I x H] + up [I x H] + down [H x I]; rows grouped by expert and
+//   low-bit storage reduce the bytes that must move.
+//
+// Work decomposition.  The permutation groups each expert's rows; a tile is
+// up to 16*NB consecutive rows of one expert.  A workgroup streams a slab of
+// weight rows of that expert exactly once from HBM and applies it to every
+// row of the tile, so an expert with <= 16*NB rows is read once per call.
+// MFMA v_mfma_f32_16x16x32_bf16 with A = activations (16 tokens) and
+// B = weights (16 weight rows): lane (r, q) = (l % 16, l / 16) loads 8
+// consecutive k of weight row r and of token row r, and the result lane holds
+// tokens 4q..4q+3 of weight row r -- so every lane's outputs share one weight
+// row, and one group scale per 32-wide k chunk serves all of them.
+//
+// Low-bit weights: one MFMA per group of 32 codes (codes -> exact bf16
+// integers), the float32 group partial is multiplied by the fp16 scale and
+// accumulated in float32.
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+enum { WF_BF16 = 0, WF_INT4 = 1, WF_INT2 = 2 };
+
+template <int WF>
+__device__ __forceinline__ size_t row_bytes(int K) {
+  return WF == WF_BF16 ? static_cast<size_t>(K) * 2 : (WF == WF_INT4 ? K / 2 : K / 4);
+}
+
+// B operand of one 32-wide k chunk starting at kk for lane chunk q.
+template <int WF>
+__device__ __forceinline__ u32x4_t load_w(const uint8_t* row, int kk, int q) {
+  if constexpr (WF == WF_BF16) {
+    return ld16(row + static_cast<size_t>(kk) * 2 + q * 16);
+  } else if constexpr (WF == WF_INT4) {
+    return dequant_int4x8(*reinterpret_cast<const uint32_t*>(row + (kk >> 1) + q * 4));
+  } else {
+    return dequant_int2x8(*reinterpret_cast<const uint16_t*>(row + (kk >> 2) + q * 2));
+  }
+}
+
+struct Tile {
+  int e, row0, rows;
+};
+
+__device__ __forceinline__ Tile read_tile(const int32_t* tiles, int t) {
+  return Tile{tiles[3 * t], tiles[3 * t + 1], tiles[3 * t + 2]};
+}
+
+// gate/up + SwiGLU.  32 intermediate rows (two 16-row MFMA blocks) of gate and
+// of up per wave.  KSPLIT == 4: the 4 waves of a workgroup share those rows
+// and split K, partial sums are added in LDS in wave order (deterministic).
+// KSPLIT == 1: each wave owns 32 rows and the full K.
+// grid (max_tiles, I / (32 * 4 / KSPLIT)), block 256.
+template <int WF, int NB, int KSPLIT>
+__global__ __launch_bounds__(256) void k_gateup(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
+    const uint16_t* __restrict__ sg, const uint16_t* __restrict__ su,
+    const int32_t* __restrict__ tiles, int max_tiles, const int32_t* __restrict__ sorted_pair,
+    int k, int H, int I, int P, uint16_t* __restrict__ h) {
+  __shared__ f32x4_t red[KSPLIT > 1 ? KSPLIT : 1][2][2][NB][64];
+  const int n_tiles = tiles[3 * max_tiles];
+  if (static_cast<int>(blockIdx.x) >= n_tiles) return;
+  const Tile tl = read_tile(tiles, blockIdx.x);
+  if (tl.rows <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, q = lane >> 4;
+  const int i0 = KSPLIT > 1 ? blockIdx.y * 32 : (blockIdx.y * 4 + wave) * 32;
+  const int kq = H / KSPLIT;
+  const int kbeg = KSPLIT > 1 ? wave * kq : 0;
+  const size_t rb = row_bytes<WF>(H);
+  const int ng = H / 32;
+
+  const uint8_t* pw[2][2];
+  const uint16_t* ps[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const size_t irow = static_cast<size_t>(tl.e) * I + i0 + mb * 16 + r;
+    pw[mb][0] = wg + irow * rb;
+    pw[mb][1] = wu + irow * rb;
+    if constexpr (WF != WF_BF16) {
+      ps[mb][0] = sg + irow * ng;
+      ps[mb][1] = su + irow * ng;
+    }
+  }
+  const uint16_t* px[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int rr = min(b * 16 + r, tl.rows - 1);
+    int p = sorted_pair[tl.row0 + rr];
+    p = min(max(p, 0), P - 1);
+    px[b] = x + static_cast<size_t>(p / k) * H + q * 8;
+  }
+
+  f32x4_t acc[2][2][NB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int gu = 0; gu < 2; ++gu)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[mb][gu][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll 2
+  for (int kk = kbeg; kk < kbeg + kq; kk += 32) {
+    u32x4_t xa[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) xa[b] = ld16(px[b] + kk);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+      for (int gu = 0; gu < 2; ++gu) {
+        const u32x4_t wv = load_w<WF>(pw[mb][gu], kk, q);
+        if constexpr (WF == WF_BF16) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[mb][gu][b] = mfma_bf16(xa[b], wv, acc[mb][gu][b]);
+        } else {
+          const float s = fp16_to_f32(ps[mb][gu][kk >> 5]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const f32x4_t pp = mfma_bf16(xa[b], wv, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[mb][gu][b][j] = fmaf(s, pp[j], acc[mb][gu][b][j]);
+          }
+        }
+      }
+    }
+  }
+
+  if constexpr (KSPLIT > 1) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int gu = 0; gu < 2; ++gu)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) red[wave][mb][gu][b][lane] = acc[mb][gu][b];
+    __syncthreads();
+    for (int idx = wave; idx < 2 * NB; idx += 4) {
+      const int mb = idx & 1, b = idx >> 1;
+      f32x4_t G = red[0][mb][0][b][lane], U = red[0][mb][1][b][lane];
+#pragma unroll
+      for (int w = 1; w < KSPLIT; ++w) {
+        G += red[w][mb][0][b][lane];
+        U += red[w][mb][1][b][lane];
+      }
+      const int i = i0 + mb * 16 + r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = b * 16 + 4 * q + j;
+        if (rr < tl.rows) h[static_cast<size_t>(tl.row0 + rr) * I + i] = f32_to_bf16(silu(G[j]) * U[j]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int i = i0 + mb * 16 + r;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rr = b * 16 + 4 * q + j;
+          if (rr < tl.rows)
+            h[static_cast<size_t>(tl.row0 + rr) * I + i] =
+                f32_to_bf16(silu(acc[mb][0][b][j]) * acc[mb][1][b][j]);
+        }
+    }
+  }
+}
+
+// down: y[row][n] = sum_i W_down[e][n][i] h[row][i].  32 output features per
+// wave (two 16-row MFMA blocks), 128 per workgroup, full K = I.
+// grid (max_tiles, H / 128), block 256.
+template <int WF, int NB>
+__global__ __launch_bounds__(256) void k_down(const uint16_t* __restrict__ h,
+                                              const uint8_t* __restrict__ wd,
+                                              const uint16_t* __restrict__ sd,
+                                              const int32_t* __restrict__ tiles, int max_tiles,
+                                              int H, int I, uint16_t* __restrict__ y) {
+  const int n_tiles = tiles[3 * max_tiles];
+  if (static_cast<int>(blockIdx.x) >= n_tiles) return;
+  const Tile tl = read_tile(tiles, blockIdx.x);
+  if (tl.rows <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, q = lane >> 4;
+  const int n0 = (blockIdx.y * 4 + wave) * 32;
+  const size_t rb = row_bytes<WF>(I);
+  const int ng = I / 32;
+  const uint8_t* pw[2];
+  const uint16_t* ps[2];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const size_t nrow = static_cast<size_t>(tl.e) * H + n0 + mb * 16 + r;
+    pw[mb] = wd + nrow * rb;
+    if constexpr (WF != WF_BF16) ps[mb] = sd + nrow * ng;
+  }
+  const uint16_t* ph[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    ph[b] = h + static_cast<size_t>(tl.row0 + min(b * 16 + r, tl.rows - 1)) * I + q * 8;
+
+  f32x4_t acc[2][NB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[mb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll 2
+  for (int kk = 0; kk < I; kk += 32) {
+    u32x4_t ha[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) ha[b] = ld16(ph[b] + kk);
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const u32x4_t wv = load_w<WF>(pw[mb], kk, q);
+      if constexpr (WF == WF_BF16) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[mb][b] = mfma_bf16(ha[b], wv, acc[mb][b]);
+      } else {
+        const float s = fp16_to_f32(ps[mb][kk >> 5]);
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const f32x4_t pp = mfma_bf16(ha[b], wv, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[mb][b][j] = fmaf(s, pp[j], acc[mb][b][j]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int n = n0 + mb * 16 + r;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = b * 16 + 4 * q + j;
+        if (rr < tl.rows) y[static_cast<size_t>(tl.row0 + rr) * H + n] = f32_to_bf16(acc[mb][b][j]);
+      }
+  }
+}
+
+// float32 path (act and weights float32): one thread per output, float32
+// fused multiply-adds in ascending k.  grid (max_tiles, ceil(N/16)),
+// block 256 = 16 rows x 16 outputs.
+__global__ __launch_bounds__(256) void k_gateup_f32(const float* __restrict__ x,
+                                                    const float* __restrict__ wg,
+                                                    const float* __restrict__ wu,
+                                                    const int32_t* __restrict__ tiles, int max_tiles,
+                                                    const int32_t* __restrict__ sorted_pair, int k,
+                                                    int H, int I, int P, float* __restrict__ h) {
+  const int n_tiles = tiles[3 * max_tiles];
+  if (static_cast<int>(blockIdx.x) >= n_tiles) return;
+  const Tile tl = read_tile(tiles, blockIdx.x);
+  const int rr = threadIdx.x >> 4, i = blockIdx.y * 16 + (threadIdx.x & 15);
+  if (rr >= tl.rows || i >= I) return;
+  const int p = min(max(sorted_pair[tl.row0 + rr], 0), P - 1);
+  const float* xp = x + static_cast<size_t>(p / k) * H;
+  const float* gp = wg + (static_cast<size_t>(tl.e) * I + i) * H;
+  const float* up = wu + (static_cast<size_t>(tl.e) * I + i) * H;
+  float g = 0.f, u = 0.f;
+  for (int c = 0; c < H; ++c) {
+    g = fmaf(gp[c], xp[c], g);
+    u = fmaf(up[c], xp[c], u);
+  }
+  h[static_cast<size_t>(tl.row0 + rr) * I + i] = silu(g) * u;
+}
+
+__global__ __launch_bounds__(256) void k_down_f32(const float* __restrict__ h,
+                                                  const float* __restrict__ wd,
+                                                  const int32_t* __restrict__ tiles, int max_tiles,
+                                                  int H, int I, float* __restrict__ y) {
+  const int n_tiles = tiles[3 * max_tiles];
+  if (static_cast<int>(blockIdx.x) >= n_tiles) return;
+  const Tile tl = read_tile(tiles, blockIdx.x);
+  const int rr = threadIdx.x >> 4, n = blockIdx.y * 16 + (threadIdx.x & 15);
+  if (rr >= tl.rows || n >= H) return;
+  const float* hp = h + static_cast<size_t>(tl.row0 + rr) * I;
+  const float* dp = wd + (static_cast<size_t>(tl.e) * H + n) * I;
+  float acc = 0.f;
+  for (int c = 0; c < I; ++c) acc = fmaf(dp[c], hp[c], acc);
+  y[static_cast<size_t>(tl.row0 + rr) * H + n] = acc;
+}
+
+template <int WF, int NB>
+static void launch_gateup_wf(const moe_shape& s, const Plan& pl, const void* x,
+                             const moe_experts& ex, const int32_t* sorted_pair,
+                             const int32_t* tiles, void* h, hipStream_t st) {
+  const int P = s.T * s.top_k;
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  uint16_t* hb = static_cast<uint16_t*>(h);
+  if (NB <= 2 || s.I % 128 != 0) {
+    hipLaunchKernelGGL((k_gateup<WF, NB, 4>), dim3(pl.max_tiles, s.I / 32), dim3(256), 0, st, xb,
+                       static_cast<const uint8_t*>(ex.gate), static_cast<const uint8_t*>(ex.up),
+                       ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair, s.top_k, s.H,
+                       s.I, P, hb);
+  } else {
+    hipLaunchKernelGGL((k_gateup<WF, NB, 1>), dim3(pl.max_tiles, s.I / 128), dim3(256), 0, st, xb,
+                       static_cast<const uint8_t*>(ex.gate), static_cast<const uint8_t*>(ex.up),
+                       ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair, s.top_k, s.H,
+                       s.I, P, hb);
+  }
+}
+
+template <int WF, int NB>
+static void launch_down_wf(const moe_shape& s, const Plan& pl, const void* h,
+                           const moe_experts& ex, const int32_t* tiles, void* y, hipStream_t st) {
+  hipLaunchKernelGGL((k_down<WF, NB>), dim3(pl.max_tiles, s.H / 128), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(h), static_cast<const uint8_t*>(ex.down),
+                     ex.down_scale, tiles, pl.max_tiles, s.H, s.I, static_cast<uint16_t*>(y));
+}
+
+template <int WF>
+static void gateup_nb(const moe_shape& s, const Plan& pl, const void* x, const moe_experts& ex,
+                      const int32_t* sp, const int32_t* tiles, void* h, hipStream_t st) {
+  switch (pl.nb) {
+    case 1: launch_gateup_wf<WF, 1>(s, pl, x, ex, sp, tiles, h, st); break;
+    case 2: launch_gateup_wf<WF, 2>(s, pl, x, ex, sp, tiles, h, st); break;
+    default: launch_gateup_wf<WF, 4>(s, pl, x, ex, sp, tiles, h, st); break;
+  }
+}
+
+template <int WF>
+static void down_nb(const moe_shape& s, const Plan& pl, const void* h, const moe_experts& ex,
+                    const int32_t* tiles, void* y, hipStream_t st) {
+  switch (pl.nb) {
+    case 1: launch_down_wf<WF, 1>(s, pl, h, ex, tiles, y, st); break;
+    case 2: launch_down_wf<WF, 2>(s, pl, h, ex, tiles, y, st); break;
+    default: launch_down_wf<WF, 4>(s, pl, h, ex, tiles, y, st); break;
+  }
+}
+
+hipError_t launch_gateup(const moe_shape& s, const Plan& pl, const void* x, const moe_experts& ex,
+                         const int32_t* sorted_pair, const int32_t* tiles, void* h,
+                         hipStream_t st) {
+  if (s.act == MOE_DT_F32) {
+    const int P = s.T * s.top_k;
+    hipLaunchKernelGGL(k_gateup_f32, dim3(pl.max_tiles, (s.I + 15) / 16), dim3(256), 0, st,
+                       static_cast<const float*>(x), static_cast<const float*>(ex.gate),
+                       static_cast<const float*>(ex.up), tiles, pl.max_tiles, sorted_pair, s.top_k,
+                       s.H, s.I, P, static_cast<float*>(h));
+  } else if (s.wfmt == MOE_WF_DENSE) {
+    gateup_nb<WF_BF16>(s, pl, x, ex, sorted_pair, tiles, h, st);
+  } else if (s.wfmt == MOE_WF_INT4_G32) {
+    gateup_nb<WF_INT4>(s, pl, x, ex, sorted_pair, tiles, h, st);
+  } else {
+    gateup_nb<WF_INT2>(s, pl, x, ex, sorted_pair, tiles, h, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_down(const moe_shape& s, const Plan& pl, const void* h, const moe_experts& ex,
+                       const int32_t* tiles, void* y, hipStream_t st) {
+  if (s.act == MOE_DT_F32) {
+    hipLaunchKernelGGL(k_down_f32, dim3(pl.max_tiles, (s.H + 15) / 16), dim3(256), 0, st,
+                       static_cast<const float*>(h), static_cast<const float*>(ex.down), tiles,
+                       pl.max_tiles, s.H, s.I, static_cast<float*>(y));
+  } else if (s.wfmt == MOE_WF_DENSE) {
+    down_nb<WF_BF16>(s, pl, h, ex, tiles, y, st);
+  } else if (s.wfmt == MOE_WF_INT4_G32) {
+    down_nb<WF_INT4>(s, pl, h, ex, tiles, y, st);
+  } else {
+    down_nb<WF_INT2>(s, pl, h, ex, tiles, y, st);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_ffn(const moe_shape& s, const Plan& pl, const void* x, const moe_experts& ex,
+                      const int32_t* sorted_pair, const int32_t* tiles, void* h, void* y,
+                      hipStream_t st) {
+  hipError_t e = launch_gateup(s, pl, x, ex, sorted_pair, tiles, h, st);
+  if (e == hipSuccess) e = launch_down(s, pl, h, ex, tiles, y, st);
+  return e;
+}
+
+}  // namespace moe

@@ -1,0 +1,394 @@
+// C ABI of the routed-MoE layer: host-side validation, launch planning and
+// dispatch.  Validation is complete before the first HIP call of an entry
+// point, so a rejected call enqueues nothing and writes nothing (the
+// fail-closed admission rule of "Agent Field Notes -- full corpus", AFN-001,
+// section "Phase 3: reject before the GPU exists").
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+static size_t act_bytes(const moe_shape& s) { return s.act == MOE_DT_F32 ? 4 : 2; }
+
+static size_t wrow_bytes(const moe_shape& s, int K) {
+  switch (s.wfmt) {
+    case MOE_WF_INT4_G32: return static_cast<size_t>(K) / 2;
+    case MOE_WF_INT2_G32: return static_cast<size_t>(K) / 4;
+    default: return static_cast<size_t>(K) * act_bytes(s);
+  }
+}
+
+bool make_plan(const moe_shape& s, Plan* p) {
+  const int64_t T = s.T, P = static_cast<int64_t>(s.T) * s.top_k;
+  std::memset(p, 0, sizeof(*p));
+  p->chunks = permute_single_pass(s) ? 0 : permute_chunks(s);
+  if (s.act == MOE_DT_F32 || T <= 16) p->nb = 1;
+  else if (T <= 1024) p->nb = 2;
+  else p->nb = 4;
+  p->max_tiles = static_cast<int>(P / (16 * p->nb) + std::min<int64_t>(s.E, P));
+
+  size_t off = 0;
+  p->logits_off = off;
+  off = align_up(off + static_cast<size_t>(T) * s.E * sizeof(float), 256);
+  p->chunk_off = off;
+  off = align_up(off + static_cast<size_t>(p->chunks) * s.E * 2 * sizeof(int32_t), 256);
+  p->perm_off = off;
+  off = align_up(off + (static_cast<size_t>(s.E) * 3 + 2 + 2 * P) * sizeof(int32_t), 256);
+  p->tiles_off = off;
+  off = align_up(off + (static_cast<size_t>(p->max_tiles) * 3 + 1) * sizeof(int32_t), 256);
+  p->h_off = off;
+  off = align_up(off + static_cast<size_t>(P) * s.I * act_bytes(s), 256);
+  p->y_off = off;
+  off = align_up(off + static_cast<size_t>(P) * s.H * act_bytes(s), 256);
+  p->total = off;
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// Validation helpers
+// ---------------------------------------------------------------------------
+
+struct Span {
+  const void* p;
+  size_t n;
+};
+
+static bool overlap(Span a, Span b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// Every output must be disjoint from every other output and every input.
+static bool any_alias(const Span* outs, int no, const Span* ins, int ni) {
+  for (int i = 0; i < no; ++i) {
+    for (int j = i + 1; j < no; ++j)
+      if (overlap(outs[i], outs[j])) return true;
+    for (int j = 0; j < ni; ++j)
+      if (overlap(outs[i], ins[j])) return true;
+  }
+  return false;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static int check_shape(const moe_shape* s) {
+  if (!s) return MOE_E_NULL;
+  if (s->flags != 0) return MOE_E_FLAGS;
+  if (s->act != MOE_DT_F32 && s->act != MOE_DT_BF16) return MOE_E_DTYPE;
+  if (s->wfmt != MOE_WF_DENSE && s->wfmt != MOE_WF_INT4_G32 && s->wfmt != MOE_WF_INT2_G32)
+    return MOE_E_FORMAT;
+  if (s->act == MOE_DT_F32 && s->wfmt != MOE_WF_DENSE) return MOE_E_FORMAT;
+  if (s->T < 0 || s->T > 131072) return MOE_E_SHAPE;
+  if (s->E < 1 || s->E > 1024 || s->top_k < 1 || s->top_k > s->E) return MOE_E_SHAPE;
+  if (s->H <= 0 || s->H > 65536 || s->H % 128 != 0) return MOE_E_SHAPE;
+  if (s->I <= 0 || s->I > 65536 || s->I % 32 != 0) return MOE_E_SHAPE;
+  const int64_t T = s->T;
+  if (T * s->top_k >= (int64_t{1} << 31)) return MOE_E_LIMIT;
+  if (T * std::max(s->E, s->H) >= (int64_t{1} << 31)) return MOE_E_LIMIT;
+  return MOE_OK;
+}
+
+static int check_ptrs(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!p) return MOE_E_NULL;
+  for (const void* p : ps)
+    if (!aligned16(p)) return MOE_E_ALIGN;
+  return MOE_OK;
+}
+
+static int check_opt_ptr(const void* p) { return (p && !aligned16(p)) ? MOE_E_ALIGN : MOE_OK; }
+
+static int check_ws(const Plan& pl, void* ws, size_t bytes) {
+  if (pl.total == 0) return MOE_OK;
+  if (!ws || bytes < pl.total) return MOE_E_WORKSPACE;
+  if (!aligned16(ws)) return MOE_E_ALIGN;
+  return MOE_OK;
+}
+
+static int check_perm(const moe_perm* pm) {
+  if (!pm) return MOE_E_NULL;
+  return check_ptrs({pm->counts, pm->offsets, pm->sorted_pair, pm->pair_row, pm->active, pm->n_active});
+}
+
+static int check_experts(const moe_shape& s, const moe_experts* ex) {
+  if (!ex) return MOE_E_NULL;
+  int st = check_ptrs({ex->gate, ex->up, ex->down});
+  if (st) return st;
+  const bool q = s.wfmt != MOE_WF_DENSE;
+  if (q) return check_ptrs({ex->gate_scale, ex->up_scale, ex->down_scale});
+  if (ex->gate_scale || ex->up_scale || ex->down_scale) return MOE_E_FORMAT;
+  return MOE_OK;
+}
+
+static void expert_spans(const moe_shape& s, const moe_experts& ex, Span* out /*[6]*/) {
+  const size_t gu = static_cast<size_t>(s.E) * s.I * wrow_bytes(s, s.H);
+  const size_t dn = static_cast<size_t>(s.E) * s.H * wrow_bytes(s, s.I);
+  const size_t gs = static_cast<size_t>(s.E) * s.I * (s.H / 32) * 2;
+  const size_t ds = static_cast<size_t>(s.E) * s.H * (s.I / 32) * 2;
+  out[0] = {ex.gate, gu};
+  out[1] = {ex.up, gu};
+  out[2] = {ex.down, dn};
+  out[3] = {ex.gate_scale, ex.gate_scale ? gs : 0};
+  out[4] = {ex.up_scale, ex.up_scale ? gs : 0};
+  out[5] = {ex.down_scale, ex.down_scale ? ds : 0};
+}
+
+static void perm_spans(const moe_shape& s, const moe_perm& pm, Span* out /*[6]*/) {
+  const size_t P = static_cast<size_t>(s.T) * s.top_k;
+  out[0] = {pm.counts, s.E * 4u};
+  out[1] = {pm.offsets, (s.E + 1) * 4u};
+  out[2] = {pm.sorted_pair, P * 4};
+  out[3] = {pm.pair_row, P * 4};
+  out[4] = {pm.active, s.E * 4u};
+  out[5] = {pm.n_active, 4};
+}
+
+static PermPtrs perm_ptrs(const moe_perm& pm) {
+  return PermPtrs{pm.counts, pm.offsets, pm.sorted_pair, pm.pair_row, pm.active, pm.n_active};
+}
+
+static PermPtrs ws_perm(const moe_shape& s, const Plan& pl, void* ws) {
+  int32_t* b = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + pl.perm_off);
+  const size_t P = static_cast<size_t>(s.T) * s.top_k;
+  PermPtrs pp;
+  pp.counts = b;
+  pp.offsets = b + s.E;
+  pp.sorted_pair = b + 2 * s.E + 1;
+  pp.pair_row = pp.sorted_pair + P;
+  pp.active = pp.pair_row + P;
+  pp.n_active = pp.active + s.E;
+  return pp;
+}
+
+static int32_t* ws_tiles(const Plan& pl, void* ws) {
+  return reinterpret_cast<int32_t*>(static_cast<char*>(ws) + pl.tiles_off);
+}
+
+static int device_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_DEVICE; }
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK) return 0;
+  if (shape->T == 0) return 0;
+  Plan pl;
+  make_plan(*shape, &pl);
+  return pl.total;
+}
+
+const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_E_NULL: return "MOE_E_NULL: a required pointer is NULL";
+    case MOE_E_SHAPE: return "MOE_E_SHAPE: dimension outside the supported domain";
+    case MOE_E_DTYPE: return "MOE_E_DTYPE: unknown activation type";
+    case MOE_E_FORMAT: return "MOE_E_FORMAT: unsupported weight format or combination";
+    case MOE_E_ALIGN: return "MOE_E_ALIGN: pointer not 16-byte aligned";
+    case MOE_E_ALIAS: return "MOE_E_ALIAS: an output overlaps another buffer";
+    case MOE_E_WORKSPACE: return "MOE_E_WORKSPACE: workspace missing or too small";
+    case MOE_E_LIMIT: return "MOE_E_LIMIT: index arithmetic would exceed 2^31";
+    case MOE_E_DEVICE: return "MOE_E_DEVICE: HIP error while enqueuing";
+    case MOE_E_FLAGS: return "MOE_E_FLAGS: unknown flag bit";
+    default: return "unknown moe status";
+  }
+}
+
+int moe_route(const moe_shape* shape, const void* x, const void* w_router, const float* router_bias,
+              int32_t* topk_ids, float* topk_w, float* logits, void* workspace,
+              size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if ((st = check_ptrs({x, w_router, topk_ids, topk_w}))) return st;
+  if ((st = check_opt_ptr(router_bias)) || (st = check_opt_ptr(logits))) return st;
+  Plan pl;
+  make_plan(s, &pl);
+  if ((st = check_ws(pl, workspace, workspace_bytes))) return st;
+  const size_t P = static_cast<size_t>(s.T) * s.top_k, ab = act_bytes(s);
+  const Span outs[] = {{topk_ids, P * 4}, {topk_w, P * 4},
+                       {logits, logits ? static_cast<size_t>(s.T) * s.E * 4 : 0},
+                       {workspace, pl.total}};
+  const Span ins[] = {{x, static_cast<size_t>(s.T) * s.H * ab},
+                      {w_router, static_cast<size_t>(s.E) * s.H * ab},
+                      {router_bias, router_bias ? s.E * 4u : 0}};
+  if (any_alias(outs, 4, ins, 3)) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  return device_status(
+      launch_route(s, pl, x, w_router, router_bias, topk_ids, topk_w, logits, workspace, stream));
+}
+
+int moe_permute(const moe_shape* shape, const int32_t* topk_ids, const moe_perm* perm,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if ((st = check_ptrs({topk_ids}))) return st;
+  if ((st = check_perm(perm))) return st;
+  Plan pl;
+  make_plan(s, &pl);
+  if ((st = check_ws(pl, workspace, workspace_bytes))) return st;
+  const size_t P = static_cast<size_t>(s.T) * s.top_k;
+  Span outs[7];
+  perm_spans(s, *perm, outs);
+  outs[6] = {workspace, pl.total};
+  const Span ins[] = {{topk_ids, P * 4}};
+  if (any_alias(outs, 7, ins, 1)) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  return device_status(
+      launch_permute(s, pl, topk_ids, perm_ptrs(*perm), ws_tiles(pl, workspace), workspace, stream));
+}
+
+int moe_grouped_ffn(const moe_shape* shape, const void* x, const moe_experts* experts,
+                    const moe_perm* perm, void* y, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if ((st = check_ptrs({x, y}))) return st;
+  if ((st = check_experts(s, experts))) return st;
+  if ((st = check_perm(perm))) return st;
+  Plan pl;
+  make_plan(s, &pl);
+  if ((st = check_ws(pl, workspace, workspace_bytes))) return st;
+  const size_t P = static_cast<size_t>(s.T) * s.top_k, ab = act_bytes(s);
+  Span ins[13];
+  ins[0] = {x, static_cast<size_t>(s.T) * s.H * ab};
+  expert_spans(s, *experts, ins + 1);
+  perm_spans(s, *perm, ins + 7);
+  const Span outs[] = {{y, P * s.H * ab}, {workspace, pl.total}};
+  if (any_alias(outs, 2, ins, 13)) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  void* h = static_cast<char*>(workspace) + pl.h_off;
+  int32_t* tiles = ws_tiles(pl, workspace);
+  hipError_t e = launch_plan_tiles(s, pl, perm_ptrs(*perm), tiles, stream);
+  if (e == hipSuccess) e = launch_ffn(s, pl, x, *experts, perm->sorted_pair, tiles, h, y, stream);
+  return device_status(e);
+}
+
+int moe_ffn_gate_up(const moe_shape* shape, const void* x, const moe_experts* experts,
+                    const moe_perm* perm, void* h, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if ((st = check_ptrs({x, h}))) return st;
+  if ((st = check_experts(s, experts))) return st;
+  if ((st = check_perm(perm))) return st;
+  Plan pl;
+  make_plan(s, &pl);
+  if ((st = check_ws(pl, workspace, workspace_bytes))) return st;
+  const size_t P = static_cast<size_t>(s.T) * s.top_k, ab = act_bytes(s);
+  Span ins[13];
+  ins[0] = {x, static_cast<size_t>(s.T) * s.H * ab};
+  expert_spans(s, *experts, ins + 1);
+  perm_spans(s, *perm, ins + 7);
+  const Span outs[] = {{h, P * s.I * ab}, {workspace, pl.total}};
+  if (any_alias(outs, 2, ins, 13)) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  return device_status(
+      launch_gateup(s, pl, x, *experts, perm->sorted_pair, ws_tiles(pl, workspace), h, stream));
+}
+
+int moe_ffn_down(const moe_shape* shape, const void* h, const moe_experts* experts, void* y,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if ((st = check_ptrs({h, y}))) return st;
+  if ((st = check_experts(s, experts))) return st;
+  Plan pl;
+  make_plan(s, &pl);
+  if ((st = check_ws(pl, workspace, workspace_bytes))) return st;
+  const size_t P = static_cast<size_t>(s.T) * s.top_k, ab = act_bytes(s);
+  Span ins[7];
+  ins[0] = {h, P * s.I * ab};
+  expert_spans(s, *experts, ins + 1);
+  const Span outs[] = {{y, P * s.H * ab}, {workspace, pl.total}};
+  if (any_alias(outs, 2, ins, 7)) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  return device_status(launch_down(s, pl, h, *experts, ws_tiles(pl, workspace), y, stream));
+}
+
+int moe_combine(const moe_shape* shape, const void* y, const int32_t* pair_row,
+                const float* topk_w, const void* residual, void* out, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if ((st = check_ptrs({y, pair_row, topk_w, out}))) return st;
+  if ((st = check_opt_ptr(residual))) return st;
+  const size_t P = static_cast<size_t>(s.T) * s.top_k, ab = act_bytes(s);
+  const Span outs[] = {{out, static_cast<size_t>(s.T) * s.H * ab}};
+  const Span ins[] = {{y, P * s.H * ab},
+                      {pair_row, P * 4},
+                      {topk_w, P * 4},
+                      {residual, residual ? static_cast<size_t>(s.T) * s.H * ab : 0}};
+  if (any_alias(outs, 1, ins, 4)) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  return device_status(launch_combine(s, y, pair_row, topk_w, residual, out, stream));
+}
+
+int moe_layer(const moe_shape* shape, const void* x, const void* w_router, const float* router_bias,
+              const moe_experts* experts, const void* residual, void* out, int32_t* topk_ids,
+              float* topk_w, const moe_perm* perm, void* workspace, size_t workspace_bytes,
+              hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if ((st = check_ptrs({x, w_router, out, topk_ids, topk_w}))) return st;
+  if ((st = check_opt_ptr(router_bias)) || (st = check_opt_ptr(residual))) return st;
+  if ((st = check_experts(s, experts))) return st;
+  if (perm && (st = check_perm(perm))) return st;
+  Plan pl;
+  make_plan(s, &pl);
+  if ((st = check_ws(pl, workspace, workspace_bytes))) return st;
+  const size_t P = static_cast<size_t>(s.T) * s.top_k, ab = act_bytes(s);
+  Span outs[10];
+  outs[0] = {out, static_cast<size_t>(s.T) * s.H * ab};
+  outs[1] = {topk_ids, P * 4};
+  outs[2] = {topk_w, P * 4};
+  outs[3] = {workspace, pl.total};
+  int no = 4;
+  if (perm) {
+    perm_spans(s, *perm, outs + 4);
+    no = 10;
+  }
+  Span ins[10];
+  ins[0] = {x, static_cast<size_t>(s.T) * s.H * ab};
+  ins[1] = {w_router, static_cast<size_t>(s.E) * s.H * ab};
+  ins[2] = {router_bias, router_bias ? s.E * 4u : 0};
+  ins[3] = {residual, residual ? static_cast<size_t>(s.T) * s.H * ab : 0};
+  expert_spans(s, *experts, ins + 4);
+  if (any_alias(outs, no, ins, 10)) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  const PermPtrs pp = perm ? perm_ptrs(*perm) : ws_perm(s, pl, workspace);
+  int32_t* tiles = ws_tiles(pl, workspace);
+  void* h = static_cast<char*>(workspace) + pl.h_off;
+  void* y = static_cast<char*>(workspace) + pl.y_off;
+  hipError_t e = launch_route(s, pl, x, w_router, router_bias, topk_ids, topk_w, nullptr, workspace,
+                              stream);
+  if (e == hipSuccess) e = launch_permute(s, pl, topk_ids, pp, tiles, workspace, stream);
+  if (e == hipSuccess) e = launch_ffn(s, pl, x, *experts, pp.sorted_pair, tiles, h, y, stream);
+  if (e == hipSuccess) e = launch_combine(s, y, pp.pair_row, topk_w, residual, out, stream);
+  return device_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal interface between the C-ABI layer (moe_abi.cpp) and the kernel
+// launchers.  Nothing here is exported.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Launch geometry and workspace layout for one shape.  Every region is
+// 256-byte aligned; moe_workspace_size() returns `total`.
+struct Plan {
+  // router
+  size_t logits_off;      // float [T][E] (when the caller passes no logits buffer)
+  // permutation
+  int chunks;             // 256-token chunks of the large-batch path (0: one pass)
+  size_t chunk_off;       // int32 chunk counts [chunks][E] + chunk bases [chunks][E]
+  size_t perm_off;        // int32 counts[E], offsets[E+1], sorted_pair[P],
+                          // pair_row[P], active[E], n_active[1]
+  // grouped FFN
+  int nb;                 // 16-row token groups per tile (rows per tile = 16*nb)
+  int max_tiles;          // upper bound on tiles: P/(16 nb) + min(E, P)
+  size_t tiles_off;       // int32 [3*max_tiles] (expert, row0, rows) + n_tiles
+  size_t h_off;           // act [P][I] SwiGLU intermediate
+  size_t y_off;           // act [P][H] expert outputs (moe_layer only)
+  size_t total;
+};
+
+bool make_plan(const moe_shape& s, Plan* p);
+
+struct PermPtrs {
+  int32_t *counts, *offsets, *sorted_pair, *pair_row, *active, *n_active;
+};
+
+// Launchers: enqueue only, return hipGetLastError().
+hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const void* w_router,
+                        const float* bias, int32_t* ids, float* w, float* logits, void* ws,
+                        hipStream_t st);
+bool permute_single_pass(const moe_shape& s);
+int permute_chunks(const moe_shape& s);
+hipError_t launch_permute(const moe_shape& s, const Plan& pl, const int32_t* ids,
+                          const PermPtrs& pp, int32_t* tiles /* may be null */, void* ws,
+                          hipStream_t st);
+hipError_t launch_plan_tiles(const moe_shape& s, const Plan& pl, const PermPtrs& pp,
+                             int32_t* tiles, hipStream_t st);
+hipError_t launch_gateup(const moe_shape& s, const Plan& pl, const void* x, const moe_experts& ex,
+                         const int32_t* sorted_pair, const int32_t* tiles, void* h,
+                         hipStream_t st);
+hipError_t launch_down(const moe_shape& s, const Plan& pl, const void* h, const moe_experts& ex,
+                       const int32_t* tiles, void* y, hipStream_t st);
+hipError_t launch_ffn(const moe_shape& s, const Plan& pl, const void* x, const moe_experts& ex,
+                      const int32_t* sorted_pair, const int32_t* tiles, void* h, void* y,
+                      hipStream_t st);
+hipError_t launch_combine(const moe_shape& s, const void* y, const int32_t* pair_row,
+                          const float* w, const void* residual, void* out, hipStream_t st);
+
+}  // namespace moe

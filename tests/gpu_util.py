@@ -1,0 +1,111 @@
+"""Helpers shared by the GPU parity tests (not a test module).
+
+Direction of data: the seeded generator makes the inputs on the device; the
+oracle reads those input bytes back and computes expected values; HIP stages
+may be fed oracle outputs (teacher forcing).  No HIP output is ever an oracle
+input."""
+from __future__ import annotations
+
+import sys
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+import sparse_moe_routed_amd as M
+from moe_inputs import MoEConfig, expert_view_to_numpy, make_layer, tensor_to_numpy_storage
+from oracle import moe_oracle as O
+
+DEV = torch.device("cuda")
+
+# output tolerances (bf16: max-abs and relative L2; float32: max-abs)
+TOL_BF16_ABS, TOL_BF16_RL2 = 2e-2, 1e-2
+TOL_F32_ABS = 1e-5
+TOL_W = 1e-5
+
+
+def say(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def np_of(t):
+    return tensor_to_numpy_storage(t)
+
+
+def decode(t, act):
+    return O.decode_act(np_of(t), act)
+
+
+def act_torch(act):
+    return torch.float32 if act == "f32" else torch.bfloat16
+
+
+def to_act_tensor(v64: np.ndarray, act: str) -> torch.Tensor:
+    """float64 values already on the activation grid -> device tensor."""
+    if act == "f32":
+        return torch.from_numpy(v64.astype(np.float32)).to(DEV)
+    bits = O.bf16_bits_of(v64)
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def i32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+@dataclass
+class Case:
+    cfg: MoEConfig
+    li: object              # LayerInputs on the device
+    x64: np.ndarray
+    wr64: np.ndarray
+    bias64: np.ndarray | None
+    ex_oracle: O.ExpertWeights
+    ex_gpu: object
+
+
+def make_case(cfg: MoEConfig, layer: int = 0, x: torch.Tensor | None = None) -> Case:
+    li = make_layer(cfg, layer=layer, device=DEV, with_x=x is None)
+    if x is not None:
+        li.x = x
+    ex = li.experts
+    V = expert_view_to_numpy
+    ex_oracle = O.ExpertWeights(cfg.wfmt, cfg.act, cfg.H, cfg.I, V(ex["gate"]), V(ex["up"]),
+                                V(ex["down"]), V(ex["gate_scale"]) if ex["gate_scale"] is not None else None,
+                                V(ex["up_scale"]) if ex["up_scale"] is not None else None,
+                                V(ex["down_scale"]) if ex["down_scale"] is not None else None)
+    ex_gpu = M.make_experts(ex["gate"], ex["up"], ex["down"], ex["gate_scale"], ex["up_scale"],
+                            ex["down_scale"])
+    bias64 = None if li.bias is None else li.bias.double().cpu().numpy()
+    return Case(cfg, li, decode(li.x, cfg.act), decode(li.w_router, cfg.act), bias64, ex_oracle, ex_gpu)
+
+
+def buffers(cfg: MoEConfig) -> M.MoELayerBuffers:
+    return M.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.I, cfg.k, cfg.act, cfg.wfmt, device=DEV)
+
+
+def check_routes(ids_gpu, w_gpu, logits64, ids_ref, w_ref, k):
+    """Bit-exact IDs except on near-tie tokens; weights within TOL_W."""
+    near = O.near_tie_tokens(logits64, k)
+    mism = (ids_gpu != ids_ref).any(axis=1)
+    bad = mism & ~near
+    assert not bad.any(), f"route mismatch on tokens without near ties: {np.nonzero(bad)[0][:8]}"
+    ok = ~mism
+    werr = float(np.abs(w_gpu[ok] - w_ref[ok]).max()) if ok.any() else 0.0
+    assert werr <= TOL_W, f"weight error {werr}"
+    return dict(mismatch=int(mism.sum()), near_ties=int(near.sum()), max_w_err=werr), ~mism
+
+
+def check_values(got64, ref64, act, what):
+    got64 = np.asarray(got64, dtype=np.float64)
+    ref64 = np.asarray(ref64, dtype=np.float64)
+    assert got64.shape == ref64.shape
+    assert np.isfinite(got64).all(), f"{what}: non-finite GPU values"
+    err = np.abs(got64 - ref64)
+    mx = float(err.max()) if err.size else 0.0
+    rl2 = float(np.linalg.norm(got64 - ref64) / max(np.linalg.norm(ref64), 1e-300)) if err.size else 0.0
+    if act == "f32":
+        assert mx <= TOL_F32_ABS, f"{what}: max-abs {mx} (rel-L2 {rl2})"
+    else:
+        assert mx <= TOL_BF16_ABS and rl2 <= TOL_BF16_RL2, f"{what}: max-abs {mx} rel-L2 {rl2}"
+    return dict(max_abs=mx, rel_l2=rl2)

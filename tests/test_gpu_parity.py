@@ -1,0 +1,403 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Stage tests feed each HIP stage the oracle's upstream outputs (teacher
+forcing) and compare element by element; end-to-end tests run the fused
+moe_layer free and compare routes (bit-exact except near ties) and outputs
+(bf16: max-abs 2e-2 and rel-L2 1e-2; float32: max-abs 1e-5; weights 1e-5).
+"""
+import numpy as np
+import pytest
+import torch
+
+import sparse_moe_routed_amd as M
+from moe_inputs import CONFIGS, make_x
+from oracle import moe_oracle as O
+from tests.gpu_util import (DEV, buffers, check_routes, check_values, decode, i32, make_case, np_of,
+                            say, to_act_tensor)
+
+pytestmark = pytest.mark.gpu
+
+C1, C2, C3, C4, C5 = (CONFIGS[i] for i in range(1, 6))
+
+# Sizes the oracle finishes in seconds that still span several tiles, ragged
+# tails, both permutation paths and every kernel variant.
+SMALL = {
+    "tiny": C1,                                                              # workload 1, full
+    "tiny_ragged": C1.with_(T=37),
+    "decode": C2,                                                            # workload 2, full
+    "bf16_ragged": C2.with_(T=37, H=256, E=100, I=96, k=7),
+    "prefill_chunked": C3.with_(T=1100, H=256, I=128),                       # chunked permute, 64-row tiles
+    "int4_small": C4.with_(T=96, H=512, E=64, I=128, k=8, layers=1),
+    "int2_small": C5.with_(T=16, H=512, E=64, I=128, layers=1),
+    "int4_many_rows": C4.with_(T=1500, H=256, E=16, I=128, k=4, layers=1),
+    "int2_ksplit_rows": C5.with_(T=600, H=384, E=24, I=96, k=3, layers=1, bias="none"),
+}
+
+_cache = {}
+
+
+def get(name):
+    if name not in _cache:
+        cfg = SMALL[name]
+        say(f"[case {name}] generate + oracle: {cfg}")
+        case = make_case(cfg)
+        res = case.x64 if cfg.residual else None
+        ref = O.moe_layer(case.x64, case.wr64, case.bias64, case.ex_oracle, cfg.k, residual=res)
+        _cache[name] = (case, ref)
+    return _cache[name]
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    M.load()
+    yield
+    _cache.clear()
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_route(name):
+    case, ref = get(name)
+    cfg = case.cfg
+    buf = buffers(cfg)
+    say(f"[case {name}] moe_route")
+    buf.route(case.li.x, case.li.w_router, case.li.bias)
+    sync()
+    lg = buf.logits.cpu().numpy().astype(np.float64)
+    dl = np.abs(lg - ref.logits)
+    assert (dl <= 1e-5 * np.maximum(1.0, np.abs(ref.logits))).all(), f"max |dlogit| {dl.max()}"
+    stats, _ = check_routes(buf.topk_ids.cpu().numpy(), buf.topk_w.cpu().numpy().astype(np.float64),
+                            ref.logits, ref.ids, ref.w, cfg.k)
+    say(f"[case {name}] routes {stats} max|dlogit| {dl.max():.3g}")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_permute(name):
+    case, ref = get(name)
+    cfg = case.cfg
+    buf = buffers(cfg)
+    say(f"[case {name}] moe_permute on oracle ids")
+    buf.permute(topk_ids=i32(ref.ids))
+    sync()
+    p = ref.perm
+    assert np.array_equal(buf.counts.cpu().numpy(), p.counts)
+    assert np.array_equal(buf.offsets.cpu().numpy(), p.offsets)
+    assert np.array_equal(buf.sorted_pair.cpu().numpy(), p.sorted_pair)
+    assert np.array_equal(buf.pair_row.cpu().numpy(), p.pair_row)
+    assert int(buf.n_active.item()) == p.n_active
+    act = buf.active.cpu().numpy()
+    assert np.array_equal(act[:p.n_active], p.active) and (act[p.n_active:] == -1).all()
+
+
+def _oracle_perm_tensors(p):
+    t = [i32(p.counts), i32(p.offsets), i32(p.sorted_pair), i32(p.pair_row),
+         i32(np.concatenate([p.active, -np.ones(len(p.counts) - p.n_active)])), i32([p.n_active])]
+    return t, M.make_perm(*t)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_grouped_ffn(name):
+    case, ref = get(name)
+    cfg = case.cfg
+    buf = buffers(cfg)
+    keep, perm = _oracle_perm_tensors(ref.perm)
+    say(f"[case {name}] moe_grouped_ffn on oracle permutation")
+    buf.grouped_ffn(case.li.x, case.ex_gpu, perm=perm)
+    sync()
+    stats = check_values(decode(buf.y, cfg.act), ref.Y, cfg.act, "Y")
+    say(f"[case {name}] Y {stats}")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_combine(name):
+    case, ref = get(name)
+    cfg = case.cfg
+    buf = buffers(cfg)
+    Yr = O.act_round(ref.Y, cfg.act)
+    w32 = ref.w.astype(np.float32)
+    res = case.li.x if cfg.residual else None
+    say(f"[case {name}] moe_combine on oracle slots")
+    buf.combine(residual=res, y=to_act_tensor(Yr, cfg.act), pair_row=i32(ref.perm.pair_row),
+                topk_w=torch.from_numpy(w32).to(DEV))
+    sync()
+    want = O.combine(Yr, ref.perm.pair_row, w32.astype(np.float64), case.x64 if cfg.residual else None)
+    stats = check_values(decode(buf.out, cfg.act), want, cfg.act, "out")
+    say(f"[case {name}] combine {stats}")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_layer_end_to_end(name):
+    case, ref = get(name)
+    cfg = case.cfg
+    buf = buffers(cfg)
+    res = case.li.x if cfg.residual else None
+    say(f"[case {name}] moe_layer")
+    buf.layer(case.li.x, case.li.w_router, case.li.bias, case.ex_gpu, residual=res)
+    sync()
+    stats, same = check_routes(buf.topk_ids.cpu().numpy(), buf.topk_w.cpu().numpy().astype(np.float64),
+                               ref.logits, ref.ids, ref.w, cfg.k)
+    got = decode(buf.out, cfg.act)
+    vs = check_values(got[same], ref.out[same], cfg.act, "out")
+    say(f"[case {name}] layer routes {stats} out {vs}")
+
+
+# --------------------------------------------------------------------------
+# Full-size workloads (sampled where the oracle cannot do every output)
+# --------------------------------------------------------------------------
+
+def _full_layer_check(cfg, layer, n_sample, seed):
+    say(f"[full {cfg.name} layer {layer}] generate")
+    case = make_case(cfg, layer=layer)
+    rng = np.random.default_rng(seed)
+    sample = np.sort(rng.choice(cfg.T, size=min(n_sample, cfg.T), replace=False))
+    res64 = case.x64 if cfg.residual else None
+    say(f"[full {cfg.name} layer {layer}] oracle (routes for all tokens, experts for {len(sample)})")
+    ref = O.moe_layer(case.x64, case.wr64, case.bias64, case.ex_oracle, cfg.k, residual=res64,
+                      only_tokens=sample)
+    buf = buffers(cfg)
+    say(f"[full {cfg.name} layer {layer}] moe_route")
+    buf.route(case.li.x, case.li.w_router, case.li.bias)
+    sync()
+    stats, _ = check_routes(buf.topk_ids.cpu().numpy(), buf.topk_w.cpu().numpy().astype(np.float64),
+                            ref.logits, ref.ids, ref.w, cfg.k)
+    say(f"[full {cfg.name} layer {layer}] routes {stats}; permute on oracle ids")
+    buf.permute(topk_ids=i32(ref.ids))
+    sync()
+    assert np.array_equal(buf.sorted_pair.cpu().numpy(), ref.perm.sorted_pair)
+    assert np.array_equal(buf.pair_row.cpu().numpy(), ref.perm.pair_row)
+    assert np.array_equal(buf.counts.cpu().numpy(), ref.perm.counts)
+    keep, perm = _oracle_perm_tensors(ref.perm)
+    say(f"[full {cfg.name} layer {layer}] grouped ffn on oracle permutation")
+    buf.grouped_ffn(case.li.x, case.ex_gpu, perm=perm)
+    sync()
+    rows = ref.perm.pair_row[(sample[:, None] * cfg.k + np.arange(cfg.k)).reshape(-1)]
+    yv = check_values(decode(buf.y, cfg.act)[rows], ref.Y[rows], cfg.act, "Y")
+    say(f"[full {cfg.name} layer {layer}] Y {yv}; fused layer")
+    res = case.li.x if cfg.residual else None
+    buf.layer(case.li.x, case.li.w_router, case.li.bias, case.ex_gpu, residual=res)
+    sync()
+    ids = buf.topk_ids.cpu().numpy()
+    same = (ids[sample] == ref.ids[sample]).all(axis=1)
+    near = O.near_tie_tokens(ref.logits[sample], cfg.k)
+    assert (same | near).all()
+    got = decode(buf.out, cfg.act)[sample]
+    ov = check_values(got[same], ref.out[sample][same], cfg.act, "out")
+    ua = int(ref.perm.n_active)
+    say(f"[full {cfg.name} layer {layer}] out {ov}; unique experts {ua}; "
+        f"repeat fraction {O.repeat_fraction(ref.ids):.3f}; max load {ref.perm.counts.max()}")
+    return ref
+
+
+def test_full_decode():
+    _full_layer_check(C2, 0, 8, 0)
+
+
+def test_full_prefill():
+    ref = _full_layer_check(C3, 0, 12, 1)
+    c = ref.perm.counts
+    assert c.max() > 10 * c[c > 0].mean()          # Zipf bias skews loads as specified
+
+
+@pytest.mark.parametrize("layer", [0, 47])
+def test_full_stack_int4_layer(layer):
+    _full_layer_check(C4, layer, 12, 2 + layer)
+
+
+@pytest.mark.parametrize("layer", [0, 47])
+def test_full_verify_int2_layer(layer):
+    ref = _full_layer_check(C5, layer, 16, 3 + layer)
+    assert O.repeat_fraction(ref.ids) > 0.5
+
+
+def test_stack_teacher_forced_int2():
+    """Layers 0..2 of the int2 verifier stack: the oracle runs the chain
+    x_{l+1} = bf16(x_l + moe_l(x_l)); the GPU layer l is fed the oracle's x_l
+    and must reproduce the oracle's x_{l+1}."""
+    cfg = C5
+    say("[stack int2] generate 3 layers")
+    cases = [make_case(cfg, layer=l) for l in range(3)]
+    xs = O.moe_stack(cases[0].x64, [(lambda c=c: (c.wr64, c.bias64, c.ex_oracle)) for c in cases],
+                     cfg.k, cfg.act)
+    buf = buffers(cfg)
+    for l, c in enumerate(cases):
+        x_l = to_act_tensor(xs[l], cfg.act)
+        say(f"[stack int2] layer {l}")
+        buf.layer(x_l, c.li.w_router, c.li.bias, c.ex_gpu, residual=x_l)
+        sync()
+        ref_r = O.moe_layer(xs[l], c.wr64, c.bias64, c.ex_oracle, cfg.k, residual=xs[l])
+        stats, same = check_routes(buf.topk_ids.cpu().numpy(),
+                                   buf.topk_w.cpu().numpy().astype(np.float64), ref_r.logits,
+                                   ref_r.ids, ref_r.w, cfg.k)
+        got = decode(buf.out, cfg.act)
+        check_values(got[same], xs[l + 1][same], cfg.act, f"x_{l + 1}")
+
+
+# --------------------------------------------------------------------------
+# Properties and edge cases
+# --------------------------------------------------------------------------
+
+def test_determinism_three_runs():
+    case, _ = get("decode")
+    cfg = case.cfg
+    outs = []
+    for i in range(3):
+        buf = buffers(cfg)
+        say(f"[determinism] run {i}")
+        buf.layer(case.li.x, case.li.w_router, case.li.bias, case.ex_gpu)
+        sync()
+        outs.append((buf.out.view(torch.int16).cpu().numpy(), buf.topk_ids.cpu().numpy(),
+                     buf.topk_w.cpu().numpy(), buf.sorted_pair.cpu().numpy()))
+    for o in outs[1:]:
+        for a, b in zip(outs[0], o):
+            assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["prefill_chunked", "int4_small", "tiny"])
+def test_fused_equals_staged(name):
+    case, _ = get(name)
+    cfg = case.cfg
+    res = case.li.x if cfg.residual else None
+    a, b = buffers(cfg), buffers(cfg)
+    say(f"[fused==staged {name}]")
+    a.layer(case.li.x, case.li.w_router, case.li.bias, case.ex_gpu, residual=res)
+    b.route(case.li.x, case.li.w_router, case.li.bias)
+    b.permute()
+    b.grouped_ffn(case.li.x, case.ex_gpu)
+    b.combine(residual=res)
+    sync()
+    for name_ in ("out", "topk_ids", "topk_w", "sorted_pair", "pair_row", "counts"):
+        ta, tb = getattr(a, name_), getattr(b, name_)
+        if ta.dtype == torch.bfloat16:
+            ta, tb = ta.view(torch.int16), tb.view(torch.int16)
+        assert torch.equal(ta, tb), name_
+
+
+def test_batch_partition_invariance():
+    """Routes of 512 tokens in one call equal those of 8 calls of 64 tokens
+    (the replay/decode route-parity requirement), bit for bit."""
+    cfg = C3.with_(T=512)
+    case = make_case(cfg)
+    whole = buffers(cfg)
+    say("[partition] whole batch")
+    whole.route(case.li.x, case.li.w_router, case.li.bias)
+    part = buffers(cfg.with_(T=64))
+    for i in range(8):
+        say(f"[partition] part {i}")
+        part.route(case.li.x[64 * i:64 * (i + 1)].contiguous(), case.li.w_router, case.li.bias)
+        sync()
+        assert torch.equal(part.topk_ids, whole.topk_ids[64 * i:64 * (i + 1)])
+        assert torch.equal(part.topk_w, whole.topk_w[64 * i:64 * (i + 1)])
+        assert torch.equal(part.logits, whole.logits[64 * i:64 * (i + 1)])
+
+
+def _small_dense(T=24, H=256, E=16, I=64, k=4):
+    return C2.with_(T=T, H=H, E=E, I=I, k=k)
+
+
+def test_zero_router_exact_ties():
+    cfg = _small_dense()
+    case = make_case(cfg)
+    buf = buffers(cfg)
+    say("[ties] zero router")
+    buf.route(case.li.x, torch.zeros_like(case.li.w_router), None)
+    sync()
+    assert (buf.topk_ids.cpu().numpy() == np.arange(cfg.k)).all()
+    assert np.allclose(buf.topk_w.cpu().numpy(), 1.0 / cfg.k, atol=1e-7)
+
+
+def test_duplicate_router_rows_lower_index_first():
+    cfg = _small_dense()
+    case = make_case(cfg)
+    wr = case.li.w_router.clone()
+    wr[9] = wr[3]
+    bias = torch.zeros(cfg.E, dtype=torch.float32, device=DEV)
+    bias[3] = bias[9] = 50.0
+    buf = buffers(cfg)
+    say("[ties] duplicate rows")
+    buf.route(case.li.x, wr, bias)
+    sync()
+    ids = buf.topk_ids.cpu().numpy()
+    assert (ids[:, 0] == 3).all() and (ids[:, 1] == 9).all()
+
+
+def test_forced_routes_by_bias():
+    cfg = _small_dense(E=40, k=5)
+    case = make_case(cfg)
+    order = [17, 2, 33, 8, 25]
+    bias = torch.zeros(cfg.E, dtype=torch.float32, device=DEV)
+    for j, e in enumerate(order):
+        bias[e] = 100.0 - 10 * j
+    buf = buffers(cfg)
+    say("[forced routes]")
+    buf.layer(case.li.x, case.li.w_router, bias, case.ex_gpu)
+    sync()
+    assert (buf.topk_ids.cpu().numpy() == np.array(order)).all()
+    assert int(buf.n_active.item()) == 5
+    ref = O.moe_layer(case.x64, case.wr64, bias.double().cpu().numpy(), case.ex_oracle, cfg.k)
+    check_values(decode(buf.out, cfg.act), ref.out, cfg.act, "out")
+
+
+def test_k_equals_E():
+    cfg = _small_dense(T=9, E=16, k=16)
+    case = make_case(cfg)
+    ref = O.moe_layer(case.x64, case.wr64, None, case.ex_oracle, cfg.k)
+    buf = buffers(cfg)
+    say("[k == E]")
+    buf.layer(case.li.x, case.li.w_router, None, case.ex_gpu)
+    sync()
+    check_routes(buf.topk_ids.cpu().numpy(), buf.topk_w.cpu().numpy().astype(np.float64),
+                 ref.logits, ref.ids, ref.w, cfg.k)
+    check_values(decode(buf.out, cfg.act), ref.out, cfg.act, "out")
+
+
+@pytest.mark.parametrize("T", [1, 2, 31, 33])
+def test_small_T(T):
+    cfg = C2.with_(T=T, H=512, E=64, I=128, k=6)
+    case = make_case(cfg)
+    ref = O.moe_layer(case.x64, case.wr64, None, case.ex_oracle, cfg.k)
+    buf = buffers(cfg)
+    say(f"[small T={T}]")
+    buf.layer(case.li.x, case.li.w_router, None, case.ex_gpu)
+    sync()
+    _, same = check_routes(buf.topk_ids.cpu().numpy(), buf.topk_w.cpu().numpy().astype(np.float64),
+                           ref.logits, ref.ids, ref.w, cfg.k)
+    check_values(decode(buf.out, cfg.act)[same], ref.out[same], cfg.act, "out")
+
+
+def test_hot_experts_many_tiles():
+    """Every token picks the same k experts: each has T rows, split into many
+    tiles, and every tile must read the right rows."""
+    cfg = C2.with_(T=300, H=256, E=32, I=64, k=3)
+    case = make_case(cfg)
+    bias = torch.zeros(cfg.E, dtype=torch.float32, device=DEV)
+    bias[[5, 6, 7]] = torch.tensor([60.0, 50.0, 40.0], device=DEV)
+    ref = O.moe_layer(case.x64, case.wr64, bias.double().cpu().numpy(), case.ex_oracle, cfg.k)
+    buf = buffers(cfg)
+    say("[hot experts]")
+    buf.layer(case.li.x, case.li.w_router, bias, case.ex_gpu)
+    sync()
+    assert (buf.counts.cpu().numpy()[[5, 6, 7]] == 300).all()
+    check_values(decode(buf.out, cfg.act), ref.out, cfg.act, "out")
+
+
+def test_max_experts():
+    cfg = C2.with_(T=40, H=256, E=1024, I=64, k=32)
+    case = make_case(cfg)
+    ref = O.moe_layer(case.x64, case.wr64, None, case.ex_oracle, cfg.k)
+    buf = buffers(cfg)
+    say("[E=1024, k=32]")
+    buf.layer(case.li.x, case.li.w_router, None, case.ex_gpu)
+    sync()
+    _, same = check_routes(buf.topk_ids.cpu().numpy(), buf.topk_w.cpu().numpy().astype(np.float64),
+                           ref.logits, ref.ids, ref.w, cfg.k)
+    check_values(decode(buf.out, cfg.act)[same], ref.out[same], cfg.act, "out")
+
+
+def test_t_zero_noop():
+    cfg = C2.with_(T=0)
+    s = M.make_shape(0, cfg.H, cfg.E, cfg.I, cfg.k)
+    assert M.moe_layer(s, None, None, None, None, None, None, None, None, None, None, 0) == 0

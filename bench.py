@@ -1,0 +1,337 @@
+#!/usr/bin/env python3
+"""Routed-MoE layer throughput on one MI355X.
+
+A step is one pass of the whole routed layer (router -> top-k -> permutation
+-> grouped gate/up + SwiGLU -> grouped down -> rank-order combine; for the
+stacked workloads all 48 layers, x_{l+1} = x_l + moe_l(x_l)) over one batch of
+synthetic tokens already resident in HBM.  Steps cycle over --batches
+distinct token batches, so the set of active experts changes from step to step
+as it does between decode batches.
+
+Prints one JSON line: tokens/s of the workload, the roofline of the dominant
+kernel (the grouped gate/up + SwiGLU kernel, timed with HIP events around
+each of its launches on the stream it runs on), and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector
+RIDGE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+WORKLOADS = {"tiny": 1, "decode": 2, "prefill": 3, "stack_int4": 4, "verify_int2": 5}
+WBYTES = {"dense": None, "int4_g32": 0.5, "int2_g32": 0.25}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 200 for one layer, 10 for 48-layer stacks)")
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode", choices=list(WORKLOADS))
+    ap.add_argument("--batches", type=int, default=16, help="distinct token batches cycled")
+    ap.add_argument("--layers", type=int, default=None, help="override the stack depth")
+    ap.add_argument("--layout", default="tiled", choices=["tiled", "row"],
+                    help="expert weight layout (tiled: converted once at load time)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (PMC calibration)")
+    return ap.parse_args()
+
+
+def weight_bytes_per_param(cfg):
+    if cfg.wfmt == "dense":
+        return 4.0 if cfg.act == "f32" else 2.0
+    return WBYTES[cfg.wfmt] + 2.0 / 32            # codes + one fp16 scale per 32
+
+
+def gateup_traffic(cfg, U):
+    """Algorithmic bytes and flops of one grouped gate/up launch: the gate and
+    up weights of the U active experts read once, the T token rows read, the
+    P x I intermediate written."""
+    act = 4 if cfg.act == "f32" else 2
+    P = cfg.T * cfg.k
+    w = U * 2 * cfg.I * cfg.H * weight_bytes_per_param(cfg)
+    b = w + cfg.T * cfg.H * act + P * cfg.I * act
+    f = 2.0 * P * 2 * cfg.I * cfg.H
+    return b, f
+
+
+def layer_bytes(cfg, U):
+    """Algorithmic bytes of one layer: active expert records once, the router
+    weight, x in and out."""
+    act = 4 if cfg.act == "f32" else 2
+    rec = 3 * cfg.I * cfg.H * weight_bytes_per_param(cfg)
+    return U * rec + cfg.E * cfg.H * act + 2 * cfg.T * cfg.H * act
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_moe_routed_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(workload, digest):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 PMC summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"gateup_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import sparse_moe_routed_amd as M
+    from moe_inputs import CONFIGS, make_experts, make_router, make_x
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": n, "launches": 5}))
+        return
+
+    M.load()
+    cfg = CONFIGS[WORKLOADS[args.workload]]
+    L = cfg.layers if args.layers is None else args.layers
+    if args.steps is None:
+        args.steps = 200 if L == 1 else 10
+    if args.warmup is None:
+        args.warmup = 20 if L == 1 else 3
+    T, k = cfg.T, cfg.k
+
+    # ---- inputs resident in HBM --------------------------------------------
+    tiled = args.layout == "tiled" and cfg.act == "bf16" and cfg.I % 128 == 0
+    row_shape = M.make_shape(T, cfg.H, cfg.E, cfg.I, k, cfg.act, cfg.wfmt)
+
+    def mk(ex):
+        return M.make_experts(ex["gate"], ex["up"], ex["down"], ex["gate_scale"], ex["up_scale"],
+                              ex["down_scale"])
+
+    layers = []
+    for l in range(L):
+        wr, bias = make_router(cfg, l, dev)
+        ex = make_experts(cfg, l, dev)
+        if tiled:   # one-time layout conversion at load time; the row-major copy is dropped
+            tex = {n: (None if t is None else torch.empty_like(t)) for n, t in ex.items()}
+            M.moe_tile_experts(row_shape, mk(ex), mk(tex))
+            torch.cuda.synchronize()
+            ex = tex
+        layers.append((wr, bias, ex, mk(ex)))
+    xs = [make_x(cfg, dev, batch=b) for b in range(args.batches)]
+    buf = M.MoELayerBuffers(T, cfg.H, cfg.E, cfg.I, k, cfg.act, cfg.wfmt, device=dev, tiled=tiled)
+    acts = [torch.empty_like(xs[0]) for _ in range(2)]
+    torch.cuda.synchronize()
+
+    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * L)]
+    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * L)]
+
+    def step(i, timed_idx=None):
+        x = xs[i % len(xs)]
+        for l, (wr, bias, _, exg) in enumerate(layers):
+            out = acts[l % 2] if L > 1 else buf.out
+            buf.route(x, wr, bias, logits=False)
+            buf.permute()
+            if timed_idx is not None:
+                ev_a[timed_idx * L + l].record()
+            buf.ffn_gate_up(x, exg)
+            if timed_idx is not None:
+                ev_b[timed_idx * L + l].record()
+            buf.ffn_down(exg)
+            buf.combine(residual=x if cfg.residual else None, out=out)
+            x = out
+
+    # ---- routing statistics per (batch, layer), untimed ---------------------
+    U = np.zeros((len(xs), L), dtype=np.int64)
+    for b in range(len(xs)):
+        x = xs[b]
+        for l, (wr, bias, _, exg) in enumerate(layers):
+            out = acts[l % 2] if L > 1 else buf.out
+            buf.route(x, wr, bias, logits=False)
+            buf.permute()
+            U[b, l] = int(buf.n_active.item())
+            buf.ffn_gate_up(x, exg)
+            buf.ffn_down(exg)
+            buf.combine(residual=x if cfg.residual else None, out=out)
+            x = out
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(args.steps):
+        step(i, timed_idx=i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    elapsed_ms = t_start.elapsed_time(t_end)
+    ms_per_step = elapsed_ms / args.steps
+    tokens_per_s = T * args.steps / (elapsed_ms / 1e3)
+
+    # ---- dominant kernel roofline --------------------------------------------
+    gu_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
+    gu_bytes = np.zeros(args.steps * L)
+    gu_flops = np.zeros(args.steps * L)
+    for i in range(args.steps):
+        for l in range(L):
+            gu_bytes[i * L + l], gu_flops[i * L + l] = gateup_traffic(cfg, U[i % len(xs), l])
+    avg_ms = float(gu_ms.mean())
+    avg_bytes = float(gu_bytes.mean())
+    avg_flops = float(gu_flops.mean())
+    intensity = avg_flops / avg_bytes
+    if cfg.act == "f32":
+        bound, peak, unit = "alu", FP32_PEAK_TFLOPS, "TFLOP/s"
+        achieved = avg_flops / (avg_ms / 1e3) / 1e12
+    elif intensity > RIDGE:
+        bound, peak, unit = "mfma", BF16_PEAK_TFLOPS, "TFLOP/s"
+        achieved = avg_flops / (avg_ms / 1e3) / 1e12
+    else:
+        bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
+        achieved = avg_bytes / (avg_ms / 1e3) / 1e9
+    digest = kernel_source_digest()
+    traffic = traffic_from_profiles(args.workload, digest)
+
+    step_bytes = np.mean([sum(layer_bytes(cfg, U[b, l]) for l in range(L)) for b in range(len(xs))])
+
+    # ---- CPU oracle on a bounded sample --------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        del buf
+        cpu = cpu_baseline(cfg, L, layers, xs, args.cpu_seconds, dev)
+
+    line = {
+        "metric": "routed-MoE layer tokens/s",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.act == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": T, "H": cfg.H, "E": cfg.E, "I": cfg.I, "top_k": k,
+                   "layers": L, "weights": cfg.wfmt if cfg.wfmt != "dense" else cfg.act,
+                   "weight_layout": "tiled" if tiled else "row-major",
+                   "batches_cycled": len(xs), "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": "k_gateup (grouped gate/up + SwiGLU)",
+                     "avg_launch_us": round(avg_ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": round(avg_bytes),
+                     "flops_per_launch": round(avg_flops), "kernel_source_digest": digest},
+        "layer_hbm": {"bytes_per_step": round(step_bytes),
+                      "achieved_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
+                      "frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "mean_unique_experts_per_layer": round(float(U.mean()), 2)},
+        "cpu_baseline": cpu,
+        "host_wall_s": round(wall, 3),
+    }
+    print(json.dumps(line))
+
+
+def cpu_baseline(cfg, L, layers, xs, budget_s, dev):
+    """The CPU oracle, untuned, on a bounded sample of the same workload: whole
+    batches of the first layer(s), until the budget is spent.  Stacked
+    workloads are extrapolated from the layers sampled (tokens/s = T /
+    (mean seconds per layer * layers)).  The oracle reads row-major weights,
+    regenerated from the same seeds (the device may hold the tiled copy)."""
+    import threadpoolctl
+    import torch
+
+    from moe_inputs import make_experts
+    from moe_inputs import tensor_to_numpy_storage as npy
+    from oracle import moe_oracle as O
+
+    threads = os.cpu_count() or 1
+    layer_s, tokens = [], 0
+    t_budget = time.perf_counter()
+    with threadpoolctl.threadpool_limits(threads):
+        for b in range(len(xs)):
+            x64 = O.decode_act(npy(xs[b]), cfg.act)
+            for l in range(L):
+                wr, bias, _, _ = layers[l]
+                ex = make_experts(cfg, l, dev)
+                wr64 = O.decode_act(npy(wr), cfg.act)
+                b64 = None if bias is None else bias.double().cpu().numpy()
+                # host copies of the experts this batch selects (copies are not timed)
+                ids = O.select_topk(O.router_logits(x64, wr64, b64), cfg.k)
+                need = np.unique(ids)
+                host = {n: {int(e): npy(ex[n][int(e)]) for e in need} if ex[n] is not None else None
+                        for n in ("gate", "up", "down", "gate_scale", "up_scale", "down_scale")}
+                oex = O.ExpertWeights(cfg.wfmt, cfg.act, cfg.H, cfg.I, host["gate"], host["up"],
+                                      host["down"], host["gate_scale"], host["up_scale"],
+                                      host["down_scale"])
+                del ex
+                torch.cuda.empty_cache()
+                c0, t0 = time.process_time(), time.perf_counter()
+                r = O.moe_layer(x64, wr64, b64, oex, cfg.k, residual=x64 if cfg.residual else None)
+                x64 = O.act_round(r.out, cfg.act)
+                layer_s.append((time.perf_counter() - t0, time.process_time() - c0))
+                if time.perf_counter() - t_budget > budget_s:
+                    break
+            tokens += cfg.T
+            if time.perf_counter() - t_budget > budget_s:
+                break
+    wall = sum(w for w, _ in layer_s)
+    cpu_t = sum(c for _, c in layer_s)
+    per_layer = wall / len(layer_s)
+    return {"value": round(cfg.T / (per_layer * L), 3), "unit": "tokens/s",
+            "cores": threads, "avg_busy_threads": round(cpu_t / wall, 2), "kind": "oracle",
+            "sample": f"{len(layer_s)} layer passes of {cfg.T} tokens (float64 numpy oracle, "
+                      f"{'extrapolated to ' + str(L) + ' layers' if L > 1 else 'whole layer'}); "
+                      f"host copies of the selected experts excluded"}
+
+
+if __name__ == "__main__":
+    main()

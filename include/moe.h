@@ -42,7 +42,9 @@
  *   0 <= T <= 131072 (T == 0 is a no-op returning MOE_OK),
  *   1 <= top_k <= E <= 1024,
  *   H > 0 with H % 128 == 0, I > 0 with I % 32 == 0, H, I <= 65536,
- *   T * top_k < 2^31 and T * max(E, H) < 2^31.
+ *   T * top_k < 2^31, T * max(E, H) < 2^31, and the FFN tile count bound
+ *   T*top_k/(16*nb) + min(E, T*top_k) <= 65535 (nb = 1 for T <= 16 or float32,
+ *   2 for T <= 1024, else 4).
  * Formats (MOE_E_DTYPE / MOE_E_FORMAT otherwise):
  *   act MOE_DT_F32  with wfmt MOE_WF_DENSE (float32 weights);
  *   act MOE_DT_BF16 with wfmt MOE_WF_DENSE (bf16 weights), MOE_WF_INT4_G32
@@ -83,6 +85,9 @@ typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
  * (int4), or in byte k/4 at bit 2*(k%4) (int2). */
 typedef enum { MOE_WF_DENSE = 0, MOE_WF_INT4_G32 = 1, MOE_WF_INT2_G32 = 2 } moe_wformat;
 
+/* moe_shape.flags bits. */
+#define MOE_F_TILED_WEIGHTS 0x1u /* expert weights in the tiled layout (moe_tile_experts) */
+
 typedef struct {
   int32_t T;       /* tokens in the batch                        */
   int32_t H;       /* hidden width                               */
@@ -91,7 +96,7 @@ typedef struct {
   int32_t top_k;   /* experts selected per token                 */
   int32_t act;     /* moe_dtype of x, W_router, dense W, Y, out   */
   int32_t wfmt;    /* moe_wformat of the expert weights          */
-  uint32_t flags;  /* reserved: must be 0                        */
+  uint32_t flags;  /* MOE_F_* bits; other bits must be 0        */
 } moe_shape;
 
 /* Expert weights, expert-major (one contiguous record per component).
@@ -109,6 +114,21 @@ typedef struct {
   const uint16_t* down_scale;
 } moe_experts;
 
+/* Tiled expert layout (MOE_F_TILED_WEIGHTS).  Same bytes as the row-major
+ * layout, reordered so that every 16-row x 32-column MFMA operand fragment is
+ * contiguous and a wave's load instruction reads one contiguous block.  For
+ * one matrix W[N][K] of one expert (gate/up: N = I, K = H; down: N = H, K = I),
+ * with nb < N/16, r < 16, q < 4, j < 8:
+ *   bf16: element W[16nb + r][32ks + 8q + j] at element index
+ *         ((nb*(K/32) + ks)*64 + 16q + r)*8 + j           (ks < K/32);
+ *   int4/int2: the 8 codes W[16nb + r][128kb + 32s + 8q + j] (j = 0..7, in
+ *         the row-major little-endian packing of 8 codes: 4 bytes for int4,
+ *         2 bytes for int2) at byte offset
+ *         ((nb*(K/128) + kb)*64 + 16q + r)*B + s*(B/4)    (kb < K/128, s < 4,
+ *         B = 16 for int4, 8 for int2);
+ *   scales: scale[16nb + r][4kb + s] at fp16 index ((nb*(K/128) + kb)*16 + r)*4 + s.
+ * Requirements: bf16 activations; I % 128 == 0 (MOE_E_SHAPE otherwise). */
+
 /* Per-expert permutation of the P = T*top_k (token, slot) pairs, pair index
  * p = t*top_k + j.  Rows of expert e are rows offsets[e] .. offsets[e+1]-1,
  * in ascending p (hence ascending token).  All arrays int32, device memory:
@@ -123,6 +143,14 @@ typedef struct {
   int32_t* active;
   int32_t* n_active;
 } moe_perm;
+
+/* Rewrite row-major expert weights (shape->flags must be 0) into the tiled
+ * layout above.  src and dst are disjoint device buffers of the same sizes;
+ * the scale pointers are NULL exactly when the format is dense.  One kernel
+ * per component, enqueued on `stream`; a one-time conversion done when the
+ * weights are loaded. */
+int moe_tile_experts(const moe_shape* shape, const moe_experts* src,
+                     const moe_experts* dst, hipStream_t stream);
 
 /* Bytes of workspace every entry point below needs for this shape (the
  * maximum over all of them, so one buffer serves every call).  Host-only,

@@ -266,18 +266,27 @@ def silu(g: np.ndarray) -> np.ndarray:
         return g / (1.0 + np.exp(-g))
 
 
-def swiglu_expert(x_rows: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
-                  w_down: np.ndarray) -> np.ndarray:
-    """One routed expert: y = W_down (silu(W_gate x) * (W_up x)).
-
-    Gate and up read the same input and are combined by SwiGLU before down
-    runs ([P-019] "Hypothesis H4").  Shapes: x_rows[m, H], W_gate/W_up[I, H],
-    W_down[H, I] (the layout whose parameter count [P-019] "Why overlap alone
-    cannot defeat the byte roofline" prints); returns y[m, H]."""
+def swiglu_intermediate(x_rows: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray) -> np.ndarray:
+    """The SwiGLU intermediate silu(W_gate x) * (W_up x): gate and up read the
+    same input and are combined before down can run ([P-019] "Hypothesis
+    H4").  x_rows[m, H], W_gate/W_up[I, H] -> a[m, I]."""
     g = x_rows @ w_gate.T
     u = x_rows @ w_up.T
-    a = silu(g) * u
-    return a @ w_down.T
+    return silu(g) * u
+
+
+def down_projection(a_rows: np.ndarray, w_down: np.ndarray) -> np.ndarray:
+    """y = W_down a for each row: a_rows[m, I], W_down[H, I] -> y[m, H]."""
+    return a_rows @ w_down.T
+
+
+def swiglu_expert(x_rows: np.ndarray, w_gate: np.ndarray, w_up: np.ndarray,
+                  w_down: np.ndarray) -> np.ndarray:
+    """One routed expert: y = W_down (silu(W_gate x) * (W_up x)).  Shapes:
+    x_rows[m, H], W_gate/W_up[I, H], W_down[H, I] (the layout whose parameter
+    count [P-019] "Why overlap alone cannot defeat the byte roofline" prints);
+    returns y[m, H]."""
+    return down_projection(swiglu_intermediate(x_rows, w_gate, w_up), w_down)
 
 
 class ExpertWeights:
@@ -309,6 +318,29 @@ class ExpertWeights:
         wd = self._dense(self.down[e], sc(self.down_scale), I)
         assert wg.shape == (I, H) and wu.shape == (I, H) and wd.shape == (H, I)
         return wg, wu, wd
+
+
+def grouped_intermediate(x: np.ndarray, perm: Permutation, k: int, experts: ExpertWeights,
+                         rows_of: Optional[np.ndarray] = None) -> np.ndarray:
+    """SwiGLU intermediates in permuted row order: A[row] = silu(W_gate x_t) *
+    (W_up x_t) for the expert and token of the row."""
+    P = perm.sorted_pair.size
+    A = np.full((P, experts.I), np.nan)
+    for e in perm.active:
+        rows = np.arange(int(perm.offsets[e]), int(perm.offsets[e + 1]))
+        wg, wu, _ = experts.expert(int(e))
+        A[rows] = swiglu_intermediate(x[perm.sorted_pair[rows] // k], wg, wu)
+    return A
+
+
+def grouped_down(A: np.ndarray, perm: Permutation, experts: ExpertWeights) -> np.ndarray:
+    """Y[row] = W_down[e(row)] A[row] in permuted row order."""
+    Y = np.full((A.shape[0], experts.H), np.nan)
+    for e in perm.active:
+        rows = np.arange(int(perm.offsets[e]), int(perm.offsets[e + 1]))
+        _, _, wd = experts.expert(int(e))
+        Y[rows] = down_projection(A[rows], wd)
+    return Y
 
 
 def grouped_ffn(x: np.ndarray, perm: Permutation, k: int, experts: ExpertWeights,

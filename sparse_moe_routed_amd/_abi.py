@@ -24,8 +24,9 @@ STATUS = {
     5: "MOE_E_ALIGN", 6: "MOE_E_ALIAS", 7: "MOE_E_WORKSPACE", 8: "MOE_E_LIMIT",
     9: "MOE_E_DEVICE", 10: "MOE_E_FLAGS",
 }
-EXPORTS = ("moe_workspace_size", "moe_status_str", "moe_route", "moe_permute",
+EXPORTS = ("moe_workspace_size", "moe_status_str", "moe_tile_experts", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_layer")
+MOE_F_TILED_WEIGHTS = 0x1
 
 
 class MoEError(RuntimeError):
@@ -69,6 +70,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_workspace_size.restype = sz
     lib.moe_status_str.argtypes = [i32]
     lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_tile_experts.argtypes = [P(moe_shape), P(moe_experts), P(moe_experts), vp]
     lib.moe_route.argtypes = [P(moe_shape), vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_permute.argtypes = [P(moe_shape), vp, P(moe_perm), vp, sz, vp]
     lib.moe_grouped_ffn.argtypes = [P(moe_shape), vp, P(moe_experts), P(moe_perm), vp, vp, sz, vp]
@@ -77,7 +79,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_combine.argtypes = [P(moe_shape), vp, vp, vp, vp, vp, vp]
     lib.moe_layer.argtypes = [P(moe_shape), vp, vp, vp, P(moe_experts), vp, vp, vp, vp,
                               P(moe_perm), vp, sz, vp]
-    for name in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down",
+    for name in ("moe_tile_experts", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down",
                  "moe_combine", "moe_layer"):
         getattr(lib, name).restype = i32
     _lib = lib
@@ -126,6 +128,12 @@ def moe_workspace_size(shape: moe_shape) -> int:
 
 def moe_status_str(status: int) -> str:
     return load().moe_status_str(status).decode()
+
+
+def moe_tile_experts(shape, src, dst, stream=None, check=True) -> int:
+    st = load().moe_tile_experts(ctypes.byref(shape), None if src is None else ctypes.byref(src),
+                                 None if dst is None else ctypes.byref(dst), stream_handle(stream))
+    return _ret(st, "moe_tile_experts", check)
 
 
 def moe_route(shape, x, w_router, router_bias, topk_ids, topk_w, logits, workspace,

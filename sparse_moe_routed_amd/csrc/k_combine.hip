@@ -28,14 +28,31 @@ __global__ __launch_bounds__(256) void k_combine_bf16(const uint16_t* __restrict
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < k; ++j) {
-    const int row = min(max(pair_row[static_cast<size_t>(t) * k + j], 0), P - 1);
-    const float wj = w[static_cast<size_t>(t) * k + j];
-    const u32x4_t v = ld16(y + static_cast<size_t>(row) * H + c * 8);
+  const int32_t* pr = pair_row + static_cast<size_t>(t) * k;
+  const float* wt = w + static_cast<size_t>(t) * k;
+  // slots in batches of 8: all index/weight loads, then all row loads, then
+  // the float32 accumulation in ascending j
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int row[8];
+    float wj[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[2 * i] = fmaf(wj, __uint_as_float(v[i] << 16), acc[2 * i]);
-      acc[2 * i + 1] = fmaf(wj, __uint_as_float(v[i] & 0xffff0000u), acc[2 * i + 1]);
+    for (int u = 0; u < 8; ++u) {
+      const int j = min(j0 + u, k - 1);
+      row[u] = min(max(pr[j], 0), P - 1);
+      wj[u] = wt[j];
+    }
+    u32x4_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = ld16(y + static_cast<size_t>(row[u]) * H + c * 8);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u < k) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] = fmaf(wj[u], __uint_as_float(v[u][i] << 16), acc[2 * i]);
+          acc[2 * i + 1] = fmaf(wj[u], __uint_as_float(v[u][i] & 0xffff0000u), acc[2 * i + 1]);
+        }
+      }
     }
   }
   if (res) {

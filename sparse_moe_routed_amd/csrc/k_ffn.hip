@@ -34,16 +34,66 @@ __device__ __forceinline__ size_t row_bytes(int K) {
   return WF == WF_BF16 ? static_cast<size_t>(K) * 2 : (WF == WF_INT4 ? K / 2 : K / 4);
 }
 
-// B operand of one 32-wide k chunk starting at kk for lane chunk q.
+// Raw weight bits of one 32-wide k chunk starting at kk for lane chunk q:
+// bf16 -> 16 bytes (8 weights), int4 -> 4 bytes (8 codes), int2 -> 2 bytes.
 template <int WF>
-__device__ __forceinline__ u32x4_t load_w(const uint8_t* row, int kk, int q) {
+struct Raw;
+template <>
+struct Raw<0> {
+  typedef u32x4_t type;
+};
+template <>
+struct Raw<1> {
+  typedef uint32_t type;
+};
+template <>
+struct Raw<2> {
+  typedef uint32_t type;
+};
+
+template <int WF>
+__device__ __forceinline__ typename Raw<WF>::type load_raw(const uint8_t* row, int kk, int q) {
   if constexpr (WF == WF_BF16) {
     return ld16(row + static_cast<size_t>(kk) * 2 + q * 16);
   } else if constexpr (WF == WF_INT4) {
-    return dequant_int4x8(*reinterpret_cast<const uint32_t*>(row + (kk >> 1) + q * 4));
+    return *reinterpret_cast<const uint32_t*>(row + (kk >> 1) + q * 4);
   } else {
-    return dequant_int2x8(*reinterpret_cast<const uint16_t*>(row + (kk >> 2) + q * 2));
+    return *reinterpret_cast<const uint16_t*>(row + (kk >> 2) + q * 2);
   }
+}
+
+template <int WF>
+__device__ __forceinline__ u32x4_t decode_raw(typename Raw<WF>::type v) {
+  if constexpr (WF == WF_BF16) {
+    return v;
+  } else if constexpr (WF == WF_INT4) {
+    return dequant_int4x8(v);
+  } else {
+    return dequant_int2x8(v);
+  }
+}
+
+// fp16 scales of groups g .. g+U-1 of one weight row (U = 1 or 4; 4 requires
+// g % 4 == 0, so the 8-byte load is aligned).
+template <int U>
+struct Scales {
+  uint16_t s[U];
+};
+
+template <int U>
+__device__ __forceinline__ Scales<U> load_scales(const uint16_t* row, int g) {
+  Scales<U> r;
+  if constexpr (U == 4) {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t*>(row + g);
+    r.s[0] = static_cast<uint16_t>(v[0]);
+    r.s[1] = static_cast<uint16_t>(v[0] >> 16);
+    r.s[2] = static_cast<uint16_t>(v[1]);
+    r.s[3] = static_cast<uint16_t>(v[1] >> 16);
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) r.s[u] = row[g + u];
+  }
+  return r;
 }
 
 struct Tile {
@@ -57,9 +107,12 @@ __device__ __forceinline__ Tile read_tile(const int32_t* tiles, int t) {
 // gate/up + SwiGLU.  32 intermediate rows (two 16-row MFMA blocks) of gate and
 // of up per wave.  KSPLIT == 4: the 4 waves of a workgroup share those rows
 // and split K, partial sums are added in LDS in wave order (deterministic).
-// KSPLIT == 1: each wave owns 32 rows and the full K.
-// grid (max_tiles, I / (32 * 4 / KSPLIT)), block 256.
-template <int WF, int NB, int KSPLIT>
+// KSPLIT == 1: each wave owns 32 rows and the full K.  The k loop issues the
+// loads of U chunks of 32 before consuming them, so a wave keeps U times more
+// bytes in flight (U = 4 needs the wave's k range to be a multiple of 128).
+// grid (I / (32 * 4 / KSPLIT), max_tiles), block 256: consecutive workgroups
+// stream adjacent row slabs of the same expert.
+template <int WF, int NB, int KSPLIT, int U>
 __global__ __launch_bounds__(256) void k_gateup(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
     const uint16_t* __restrict__ sg, const uint16_t* __restrict__ su,
@@ -67,12 +120,12 @@ __global__ __launch_bounds__(256) void k_gateup(
     int k, int H, int I, int P, uint16_t* __restrict__ h) {
   __shared__ f32x4_t red[KSPLIT > 1 ? KSPLIT : 1][2][2][NB][64];
   const int n_tiles = tiles[3 * max_tiles];
-  if (static_cast<int>(blockIdx.x) >= n_tiles) return;
-  const Tile tl = read_tile(tiles, blockIdx.x);
+  if (static_cast<int>(blockIdx.y) >= n_tiles) return;
+  const Tile tl = read_tile(tiles, blockIdx.y);
   if (tl.rows <= 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
-  const int i0 = KSPLIT > 1 ? blockIdx.y * 32 : (blockIdx.y * 4 + wave) * 32;
+  const int i0 = KSPLIT > 1 ? blockIdx.x * 32 : (blockIdx.x * 4 + wave) * 32;
   const int kq = H / KSPLIT;
   const int kbeg = KSPLIT > 1 ? wave * kq : 0;
   const size_t rb = row_bytes<WF>(H);
@@ -107,26 +160,43 @@ __global__ __launch_bounds__(256) void k_gateup(
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[mb][gu][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll 2
-  for (int kk = kbeg; kk < kbeg + kq; kk += 32) {
-    u32x4_t xa[NB];
+  for (int kk = kbeg; kk < kbeg + kq; kk += 32 * U) {
+    Scales<U> sc[2][2];
+    if constexpr (WF != WF_BF16) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) xa[b] = ld16(px[b] + kk);
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+        for (int gu = 0; gu < 2; ++gu) sc[mb][gu] = load_scales<U>(ps[mb][gu], kk >> 5);
+    }
+    u32x4_t xa[U][NB];
+    typename Raw<WF>::type raw[U][2][2];
 #pragma unroll
-      for (int gu = 0; gu < 2; ++gu) {
-        const u32x4_t wv = load_w<WF>(pw[mb][gu], kk, q);
-        if constexpr (WF == WF_BF16) {
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
-          for (int b = 0; b < NB; ++b) acc[mb][gu][b] = mfma_bf16(xa[b], wv, acc[mb][gu][b]);
-        } else {
-          const float s = fp16_to_f32(ps[mb][gu][kk >> 5]);
+      for (int b = 0; b < NB; ++b) xa[u][b] = ld16(px[b] + kk + 32 * u);
 #pragma unroll
-          for (int b = 0; b < NB; ++b) {
-            const f32x4_t pp = mfma_bf16(xa[b], wv, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[mb][gu][b][j] = fmaf(s, pp[j], acc[mb][gu][b][j]);
+        for (int gu = 0; gu < 2; ++gu) raw[u][mb][gu] = load_raw<WF>(pw[mb][gu], kk + 32 * u, q);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int gu = 0; gu < 2; ++gu) {
+          const u32x4_t wv = decode_raw<WF>(raw[u][mb][gu]);
+          if constexpr (WF == WF_BF16) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[mb][gu][b] = mfma_bf16(xa[u][b], wv, acc[mb][gu][b]);
+          } else {
+            const float s = fp16_to_f32(sc[mb][gu].s[u]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const f32x4_t pp = mfma_bf16(xa[u][b], wv, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[mb][gu][b][j] = fmaf(s, pp[j], acc[mb][gu][b][j]);
+            }
           }
         }
       }
@@ -143,17 +213,17 @@ __global__ __launch_bounds__(256) void k_gateup(
     __syncthreads();
     for (int idx = wave; idx < 2 * NB; idx += 4) {
       const int mb = idx & 1, b = idx >> 1;
-      f32x4_t G = red[0][mb][0][b][lane], U = red[0][mb][1][b][lane];
+      f32x4_t G = red[0][mb][0][b][lane], U_ = red[0][mb][1][b][lane];
 #pragma unroll
       for (int w = 1; w < KSPLIT; ++w) {
         G += red[w][mb][0][b][lane];
-        U += red[w][mb][1][b][lane];
+        U_ += red[w][mb][1][b][lane];
       }
       const int i = i0 + mb * 16 + r;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int rr = b * 16 + 4 * q + j;
-        if (rr < tl.rows) h[static_cast<size_t>(tl.row0 + rr) * I + i] = f32_to_bf16(silu(G[j]) * U[j]);
+        if (rr < tl.rows) h[static_cast<size_t>(tl.row0 + rr) * I + i] = f32_to_bf16(silu(G[j]) * U_[j]);
       }
     }
   } else {
@@ -174,21 +244,22 @@ __global__ __launch_bounds__(256) void k_gateup(
 }
 
 // down: y[row][n] = sum_i W_down[e][n][i] h[row][i].  32 output features per
-// wave (two 16-row MFMA blocks), 128 per workgroup, full K = I.
-// grid (max_tiles, H / 128), block 256.
-template <int WF, int NB>
+// wave (two 16-row MFMA blocks), 128 per workgroup, full K = I, loads of U
+// k chunks issued before they are consumed (U = 4 needs I % 128 == 0).
+// grid (H / 128, max_tiles), block 256.
+template <int WF, int NB, int U>
 __global__ __launch_bounds__(256) void k_down(const uint16_t* __restrict__ h,
                                               const uint8_t* __restrict__ wd,
                                               const uint16_t* __restrict__ sd,
                                               const int32_t* __restrict__ tiles, int max_tiles,
                                               int H, int I, uint16_t* __restrict__ y) {
   const int n_tiles = tiles[3 * max_tiles];
-  if (static_cast<int>(blockIdx.x) >= n_tiles) return;
-  const Tile tl = read_tile(tiles, blockIdx.x);
+  if (static_cast<int>(blockIdx.y) >= n_tiles) return;
+  const Tile tl = read_tile(tiles, blockIdx.y);
   if (tl.rows <= 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
-  const int n0 = (blockIdx.y * 4 + wave) * 32;
+  const int n0 = (blockIdx.x * 4 + wave) * 32;
   const size_t rb = row_bytes<WF>(I);
   const int ng = I / 32;
   const uint8_t* pw[2];
@@ -210,24 +281,283 @@ __global__ __launch_bounds__(256) void k_down(const uint16_t* __restrict__ h,
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[mb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll 2
-  for (int kk = 0; kk < I; kk += 32) {
-    u32x4_t ha[NB];
+  for (int kk = 0; kk < I; kk += 32 * U) {
+    Scales<U> sc[2];
+    if constexpr (WF != WF_BF16) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) ha[b] = ld16(ph[b] + kk);
+      for (int mb = 0; mb < 2; ++mb) sc[mb] = load_scales<U>(ps[mb], kk >> 5);
+    }
+    u32x4_t ha[U][NB];
+    typename Raw<WF>::type raw[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) ha[u][b] = ld16(ph[b] + kk + 32 * u);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) raw[u][mb] = load_raw<WF>(pw[mb], kk + 32 * u, q);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4_t wv = decode_raw<WF>(raw[u][mb]);
+        if constexpr (WF == WF_BF16) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[mb][b] = mfma_bf16(ha[u][b], wv, acc[mb][b]);
+        } else {
+          const float s = fp16_to_f32(sc[mb].s[u]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const f32x4_t pp = mfma_bf16(ha[u][b], wv, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[mb][b][j] = fmaf(s, pp[j], acc[mb][b][j]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    const int n = n0 + mb * 16 + r;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = b * 16 + 4 * q + j;
+        if (rr < tl.rows) y[static_cast<size_t>(tl.row0 + rr) * H + n] = f32_to_bf16(acc[mb][b][j]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled weights (MOE_F_TILED_WEIGHTS).  The unit of the k loop is 128 k = 4
+// MFMA chunks; for one 16-row block a lane fetches, per unit, 4 x 16 B (bf16:
+// four consecutive 1 KB fragments), 16 B (int4) or 8 B (int2), plus 8 B of
+// scales, so every load instruction of a wave reads one contiguous block.
+// ---------------------------------------------------------------------------
+template <int WF>
+struct TRaw {
+  u32x4_t v[WF == WF_BF16 ? 4 : 1];
+};
+
+// Row block nb (global over the expert-concatenated matrix), k unit kb.
+template <int WF>
+__device__ __forceinline__ TRaw<WF> tload(const uint8_t* mat, size_t nb, int K, int kb, int lane) {
+  TRaw<WF> t;
+  if constexpr (WF == WF_BF16) {
+    const size_t frag = nb * static_cast<size_t>(K / 32) + 4 * static_cast<size_t>(kb);
+#pragma unroll
+    for (int f = 0; f < 4; ++f) t.v[f] = ld16(mat + ((frag + f) * 64 + lane) * 16);
+  } else if constexpr (WF == WF_INT4) {
+    t.v[0] = ld16(mat + ((nb * static_cast<size_t>(K / 128) + kb) * 64 + lane) * 16);
+  } else {
+    const u32x2_t d = *reinterpret_cast<const u32x2_t*>(
+        mat + ((nb * static_cast<size_t>(K / 128) + kb) * 64 + lane) * 8);
+    t.v[0] = u32x4_t{d[0], d[1], 0u, 0u};
+  }
+  return t;
+}
+
+template <int WF>
+__device__ __forceinline__ u32x4_t tdecode(const TRaw<WF>& t, int s) {
+  if constexpr (WF == WF_BF16) {
+    return t.v[s];
+  } else if constexpr (WF == WF_INT4) {
+    return dequant_int4x8(t.v[0][s]);
+  } else {
+    const uint32_t d = t.v[0][s >> 1];
+    return dequant_int2x8((s & 1) ? (d >> 16) : (d & 0xffffu));
+  }
+}
+
+__device__ __forceinline__ Scales<4> tscales(const uint16_t* sc, size_t nb, int K, int kb, int r) {
+  return load_scales<4>(sc + ((nb * static_cast<size_t>(K / 128) + kb) * 16 + r) * 4, 0);
+}
+
+// gate/up + SwiGLU on tiled weights.  A workgroup has 4 waves = (4/KSPLIT)
+// row groups x KSPLIT k parts; each row group is 32 intermediate rows of gate
+// and of up; the k parts of a row group are added in LDS in part order.
+// grid (I / (32 * 4 / KSPLIT), max_tiles), block 256.
+template <int WF, int NB, int KSPLIT>
+__global__ __launch_bounds__(256) void k_gateup_t(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
+    const uint16_t* __restrict__ sg, const uint16_t* __restrict__ su,
+    const int32_t* __restrict__ tiles, int max_tiles, const int32_t* __restrict__ sorted_pair,
+    int k, int H, int I, int P, uint16_t* __restrict__ h) {
+  constexpr int RG = 4 / KSPLIT;
+  __shared__ f32x4_t red[KSPLIT > 1 ? 4 : 1][2][2][NB][64];
+  const int n_tiles = tiles[3 * max_tiles];
+  if (static_cast<int>(blockIdx.y) >= n_tiles) return;
+  const Tile tl = read_tile(tiles, blockIdx.y);
+  if (tl.rows <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, q = lane >> 4;
+  const int kp = wave % KSPLIT, rg = wave / KSPLIT;
+  const int i0 = (blockIdx.x * RG + rg) * 32;
+  const int units = H / 128 / KSPLIT;
+  const int ub = kp * units;
+  const size_t nb0 = (static_cast<size_t>(tl.e) * I + i0) / 16;
+
+  const uint16_t* px[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    const int rr = min(b * 16 + r, tl.rows - 1);
+    int p = sorted_pair[tl.row0 + rr];
+    p = min(max(p, 0), P - 1);
+    px[b] = x + static_cast<size_t>(p / k) * H + q * 8;
+  }
+
+  f32x4_t acc[2][2][NB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int gu = 0; gu < 2; ++gu)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[mb][gu][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int u = ub; u < ub + units; ++u) {
+    Scales<4> sc[2][2];
+    if constexpr (WF != WF_BF16) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        sc[mb][0] = tscales(sg, nb0 + mb, H, u, r);
+        sc[mb][1] = tscales(su, nb0 + mb, H, u, r);
+      }
+    }
+    TRaw<WF> raw[2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const u32x4_t wv = load_w<WF>(pw[mb], kk, q);
-      if constexpr (WF == WF_BF16) {
+      raw[mb][0] = tload<WF>(wg, nb0 + mb, H, u, lane);
+      raw[mb][1] = tload<WF>(wu, nb0 + mb, H, u, lane);
+    }
+    u32x4_t xa[4][NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[mb][b] = mfma_bf16(ha[b], wv, acc[mb][b]);
-      } else {
-        const float s = fp16_to_f32(ps[mb][kk >> 5]);
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const f32x4_t pp = mfma_bf16(ha[b], wv, f32x4_t{0.f, 0.f, 0.f, 0.f});
+      for (int b = 0; b < NB; ++b) xa[st][b] = ld16(px[b] + 128 * u + 32 * st);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[mb][b][j] = fmaf(s, pp[j], acc[mb][b][j]);
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int gu = 0; gu < 2; ++gu) {
+          const u32x4_t wv = tdecode<WF>(raw[mb][gu], st);
+          if constexpr (WF == WF_BF16) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[mb][gu][b] = mfma_bf16(xa[st][b], wv, acc[mb][gu][b]);
+          } else {
+            const float sv = fp16_to_f32(sc[mb][gu].s[st]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const f32x4_t pp = mfma_bf16(xa[st][b], wv, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[mb][gu][b][j] = fmaf(sv, pp[j], acc[mb][gu][b][j]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  if constexpr (KSPLIT > 1) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int gu = 0; gu < 2; ++gu)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) red[wave][mb][gu][b][lane] = acc[mb][gu][b];
+    __syncthreads();
+    for (int idx = wave; idx < RG * 2 * NB; idx += 4) {
+      const int g_ = idx / (2 * NB), rem = idx % (2 * NB);
+      const int mb = rem & 1, b = rem >> 1;
+      f32x4_t G = red[g_ * KSPLIT][mb][0][b][lane], U_ = red[g_ * KSPLIT][mb][1][b][lane];
+#pragma unroll
+      for (int w = 1; w < KSPLIT; ++w) {
+        G += red[g_ * KSPLIT + w][mb][0][b][lane];
+        U_ += red[g_ * KSPLIT + w][mb][1][b][lane];
+      }
+      const int i = (blockIdx.x * RG + g_) * 32 + mb * 16 + r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = b * 16 + 4 * q + j;
+        if (rr < tl.rows) h[static_cast<size_t>(tl.row0 + rr) * I + i] = f32_to_bf16(silu(G[j]) * U_[j]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const int i = i0 + mb * 16 + r;
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rr = b * 16 + 4 * q + j;
+          if (rr < tl.rows)
+            h[static_cast<size_t>(tl.row0 + rr) * I + i] =
+                f32_to_bf16(silu(acc[mb][0][b][j]) * acc[mb][1][b][j]);
+        }
+    }
+  }
+}
+
+// down on tiled weights: 32 output features per wave, 128 per workgroup,
+// full K = I.  grid (H / 128, max_tiles), block 256.
+template <int WF, int NB>
+__global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
+                                                const uint8_t* __restrict__ wd,
+                                                const uint16_t* __restrict__ sd,
+                                                const int32_t* __restrict__ tiles, int max_tiles,
+                                                int H, int I, uint16_t* __restrict__ y) {
+  const int n_tiles = tiles[3 * max_tiles];
+  if (static_cast<int>(blockIdx.y) >= n_tiles) return;
+  const Tile tl = read_tile(tiles, blockIdx.y);
+  if (tl.rows <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, q = lane >> 4;
+  const int n0 = (blockIdx.x * 4 + wave) * 32;
+  const size_t nb0 = (static_cast<size_t>(tl.e) * H + n0) / 16;
+  const uint16_t* ph[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    ph[b] = h + static_cast<size_t>(tl.row0 + min(b * 16 + r, tl.rows - 1)) * I + q * 8;
+
+  f32x4_t acc[2][NB];
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[mb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int units = I / 128;
+  for (int u = 0; u < units; ++u) {
+    Scales<4> sc[2];
+    if constexpr (WF != WF_BF16) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) sc[mb] = tscales(sd, nb0 + mb, I, u, r);
+    }
+    TRaw<WF> raw[2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) raw[mb] = tload<WF>(wd, nb0 + mb, I, u, lane);
+    u32x4_t ha[4][NB];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) ha[st][b] = ld16(ph[b] + 128 * u + 32 * st);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const u32x4_t wv = tdecode<WF>(raw[mb], st);
+        if constexpr (WF == WF_BF16) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[mb][b] = mfma_bf16(ha[st][b], wv, acc[mb][b]);
+        } else {
+          const float sv = fp16_to_f32(sc[mb].s[st]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const f32x4_t pp = mfma_bf16(ha[st][b], wv, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[mb][b][j] = fmaf(sv, pp[j], acc[mb][b][j]);
+          }
         }
       }
     }
@@ -294,30 +624,75 @@ static void launch_gateup_wf(const moe_shape& s, const Plan& pl, const void* x,
   const int P = s.T * s.top_k;
   const uint16_t* xb = static_cast<const uint16_t*>(x);
   uint16_t* hb = static_cast<uint16_t*>(h);
+  const uint8_t* g8 = static_cast<const uint8_t*>(ex.gate);
+  const uint8_t* u8 = static_cast<const uint8_t*>(ex.up);
   if (NB <= 2 || s.I % 128 != 0) {
-    hipLaunchKernelGGL((k_gateup<WF, NB, 4>), dim3(pl.max_tiles, s.I / 32), dim3(256), 0, st, xb,
-                       static_cast<const uint8_t*>(ex.gate), static_cast<const uint8_t*>(ex.up),
-                       ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair, s.top_k, s.H,
-                       s.I, P, hb);
+    const dim3 grid(s.I / 32, pl.max_tiles);
+    if ((s.H / 4) % 128 == 0)
+      hipLaunchKernelGGL((k_gateup<WF, NB, 4, 4>), grid, dim3(256), 0, st, xb, g8, u8, ex.gate_scale,
+                         ex.up_scale, tiles, pl.max_tiles, sorted_pair, s.top_k, s.H, s.I, P, hb);
+    else
+      hipLaunchKernelGGL((k_gateup<WF, NB, 4, 1>), grid, dim3(256), 0, st, xb, g8, u8, ex.gate_scale,
+                         ex.up_scale, tiles, pl.max_tiles, sorted_pair, s.top_k, s.H, s.I, P, hb);
   } else {
-    hipLaunchKernelGGL((k_gateup<WF, NB, 1>), dim3(pl.max_tiles, s.I / 128), dim3(256), 0, st, xb,
-                       static_cast<const uint8_t*>(ex.gate), static_cast<const uint8_t*>(ex.up),
-                       ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair, s.top_k, s.H,
-                       s.I, P, hb);
+    const dim3 grid(s.I / 128, pl.max_tiles);
+    if (s.H % 128 == 0)
+      hipLaunchKernelGGL((k_gateup<WF, NB, 1, 4>), grid, dim3(256), 0, st, xb, g8, u8, ex.gate_scale,
+                         ex.up_scale, tiles, pl.max_tiles, sorted_pair, s.top_k, s.H, s.I, P, hb);
   }
 }
 
 template <int WF, int NB>
 static void launch_down_wf(const moe_shape& s, const Plan& pl, const void* h,
                            const moe_experts& ex, const int32_t* tiles, void* y, hipStream_t st) {
-  hipLaunchKernelGGL((k_down<WF, NB>), dim3(pl.max_tiles, s.H / 128), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(h), static_cast<const uint8_t*>(ex.down),
-                     ex.down_scale, tiles, pl.max_tiles, s.H, s.I, static_cast<uint16_t*>(y));
+  const dim3 grid(s.H / 128, pl.max_tiles);
+  if (s.I % 128 == 0)
+    hipLaunchKernelGGL((k_down<WF, NB, 4>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(h),
+                       static_cast<const uint8_t*>(ex.down), ex.down_scale, tiles, pl.max_tiles, s.H,
+                       s.I, static_cast<uint16_t*>(y));
+  else
+    hipLaunchKernelGGL((k_down<WF, NB, 1>), grid, dim3(256), 0, st, static_cast<const uint16_t*>(h),
+                       static_cast<const uint8_t*>(ex.down), ex.down_scale, tiles, pl.max_tiles, s.H,
+                       s.I, static_cast<uint16_t*>(y));
+}
+
+template <int WF, int NB>
+static void launch_gateup_tiled(const moe_shape& s, const Plan& pl, const void* x,
+                                const moe_experts& ex, const int32_t* sorted_pair,
+                                const int32_t* tiles, void* h, hipStream_t st) {
+  const int P = s.T * s.top_k;
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  uint16_t* hb = static_cast<uint16_t*>(h);
+  const uint8_t* g8 = static_cast<const uint8_t*>(ex.gate);
+  const uint8_t* u8 = static_cast<const uint8_t*>(ex.up);
+  // k split across the waves of a workgroup: 4 parts for small batches when
+  // H allows (more workgroups stream at once), fewer otherwise
+  const int ksplit = (NB <= 2 && s.H % 512 == 0) ? 4 : ((NB <= 2 && s.H % 256 == 0) ? 2 : 1);
+  if (ksplit == 4)
+    hipLaunchKernelGGL((k_gateup_t<WF, NB, 4>), dim3(s.I / 32, pl.max_tiles), dim3(256), 0, st, xb,
+                       g8, u8, ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair,
+                       s.top_k, s.H, s.I, P, hb);
+  else if (ksplit == 2)
+    hipLaunchKernelGGL((k_gateup_t<WF, NB, 2>), dim3(s.I / 64, pl.max_tiles), dim3(256), 0, st, xb,
+                       g8, u8, ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair,
+                       s.top_k, s.H, s.I, P, hb);
+  else
+    hipLaunchKernelGGL((k_gateup_t<WF, NB, 1>), dim3(s.I / 128, pl.max_tiles), dim3(256), 0, st, xb,
+                       g8, u8, ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair,
+                       s.top_k, s.H, s.I, P, hb);
 }
 
 template <int WF>
 static void gateup_nb(const moe_shape& s, const Plan& pl, const void* x, const moe_experts& ex,
                       const int32_t* sp, const int32_t* tiles, void* h, hipStream_t st) {
+  if (s.flags & MOE_F_TILED_WEIGHTS) {
+    switch (pl.nb) {
+      case 1: launch_gateup_tiled<WF, 1>(s, pl, x, ex, sp, tiles, h, st); break;
+      case 2: launch_gateup_tiled<WF, 2>(s, pl, x, ex, sp, tiles, h, st); break;
+      default: launch_gateup_tiled<WF, 4>(s, pl, x, ex, sp, tiles, h, st); break;
+    }
+    return;
+  }
   switch (pl.nb) {
     case 1: launch_gateup_wf<WF, 1>(s, pl, x, ex, sp, tiles, h, st); break;
     case 2: launch_gateup_wf<WF, 2>(s, pl, x, ex, sp, tiles, h, st); break;
@@ -325,9 +700,26 @@ static void gateup_nb(const moe_shape& s, const Plan& pl, const void* x, const m
   }
 }
 
+template <int WF, int NB>
+static void launch_down_tiled(const moe_shape& s, const Plan& pl, const void* h,
+                              const moe_experts& ex, const int32_t* tiles, void* y,
+                              hipStream_t st) {
+  hipLaunchKernelGGL((k_down_t<WF, NB>), dim3(s.H / 128, pl.max_tiles), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(h), static_cast<const uint8_t*>(ex.down),
+                     ex.down_scale, tiles, pl.max_tiles, s.H, s.I, static_cast<uint16_t*>(y));
+}
+
 template <int WF>
 static void down_nb(const moe_shape& s, const Plan& pl, const void* h, const moe_experts& ex,
                     const int32_t* tiles, void* y, hipStream_t st) {
+  if (s.flags & MOE_F_TILED_WEIGHTS) {
+    switch (pl.nb) {
+      case 1: launch_down_tiled<WF, 1>(s, pl, h, ex, tiles, y, st); break;
+      case 2: launch_down_tiled<WF, 2>(s, pl, h, ex, tiles, y, st); break;
+      default: launch_down_tiled<WF, 4>(s, pl, h, ex, tiles, y, st); break;
+    }
+    return;
+  }
   switch (pl.nb) {
     case 1: launch_down_wf<WF, 1>(s, pl, h, ex, tiles, y, st); break;
     case 2: launch_down_wf<WF, 2>(s, pl, h, ex, tiles, y, st); break;

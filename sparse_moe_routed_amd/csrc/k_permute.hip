@@ -64,20 +64,17 @@ __device__ void build_bits(const int32_t* __restrict__ ids, int P, int k, int W,
   __syncthreads();
 }
 
-// Word-exclusive popcount prefixes of rows [c0, c1); one wave per expert.
+// Word-exclusive popcount prefixes of rows [c0, c1); one thread per expert
+// (rows are at most a few words long on this path).
 __device__ void build_prefix(int W, int c0, int c1, const uint32_t* bits, uint32_t* pre,
                              int* s_cnt) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int e = c0 + wave; e < c1; e += 16) {
+  for (int e = c0 + static_cast<int>(threadIdx.x); e < c1; e += blockDim.x) {
     int count = 0;
-    for (int w0 = 0; w0 < W; w0 += 64) {
-      const int wi = w0 + lane;
-      const int pc = wi < W ? __popc(bits[(e - c0) * W + wi]) : 0;
-      const int inc = wave_incl_scan(pc);
-      if (wi < W) pre[(e - c0) * W + wi] = static_cast<uint32_t>(count + inc - pc);
-      count += __shfl(inc, 63, kWave);
+    for (int wi = 0; wi < W; ++wi) {
+      pre[(e - c0) * W + wi] = static_cast<uint32_t>(count);
+      count += __popc(bits[(e - c0) * W + wi]);
     }
-    if (lane == 0) s_cnt[e] = count;
+    s_cnt[e] = count;
   }
   __syncthreads();
 }

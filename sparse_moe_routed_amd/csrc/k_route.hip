@@ -14,36 +14,53 @@
 
 namespace moe {
 
-// bf16 router: one 16-expert x 16-token tile per workgroup; wave w sums the
-// K quarter [w H/4, (w+1) H/4).  Each v_mfma_f32_16x16x32_bf16 sums 32 exact
-// bf16 products in float32; those chunk sums are accumulated in float64 in k
-// order, the four quarter sums are added in wave order, the bias is added,
-// and the total is rounded once to float32.  The association is the same
-// for every token and every batch size, so a token's logits do not depend on
-// which other tokens share the call.
-// grid (ceil(T/16), ceil(E/16)), block 256.
-__global__ __launch_bounds__(256) void k_router_bf16(const uint16_t* __restrict__ x,
-                                                     const uint16_t* __restrict__ wr,
-                                                     const float* __restrict__ bias, int T, int H,
-                                                     int E, float* __restrict__ logits) {
-  __shared__ double red[4][64][4];
+// bf16 router.  The dot product over H is cut into `nparts` parts of
+// `cpp` chunks of 32 (nparts = the largest divisor of H/32 that is <= 16, so
+// the cut depends on H alone).  Each v_mfma_f32_16x16x32_bf16 sums the 32
+// exact bf16 products of a chunk in float32; the chunk sums of a part are
+// added in float64 in k order, the part sums are added in part order, the
+// bias is added, and the total is rounded once to float32.  Both kernels
+// below use exactly this association, so a token's logits are bit-identical
+// whatever the batch size or the kernel that computed them.
+constexpr int kRouterBatch = 8;
+
+// Small batches: one 16-token x 16-expert tile per workgroup, one wave per
+// part, part sums combined through LDS.  grid (ceil(T/16), ceil(E/16)),
+// block 64 * nparts.
+__global__ __launch_bounds__(1024) void k_router_parts(const uint16_t* __restrict__ x,
+                                                       const uint16_t* __restrict__ wr,
+                                                       const float* __restrict__ bias, int T,
+                                                       int H, int E, int nparts,
+                                                       float* __restrict__ logits) {
+  __shared__ double red[16][64][4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
   const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
-  const int kq = H >> 2;
-  const int kbeg = wave * kq;
+  const int cpp = H / 32 / nparts;
+  const int kbeg = wave * cpp * 32;
   const int tt = min(t0 + r, T - 1);
   const int ee = min(e0 + r, E - 1);
   const uint16_t* xp = x + static_cast<size_t>(tt) * H + kbeg + q * 8;
   const uint16_t* wp = wr + static_cast<size_t>(ee) * H + kbeg + q * 8;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  for (int kk = 0; kk < kq; kk += 32) {
-    const u32x4_t a = ld16(wp + kk);
-    const u32x4_t b = ld16(xp + kk);
-    const f32x4_t c = mfma_bf16(a, b, zero);
+  for (int c = 0; c < cpp; c += kRouterBatch) {
+    u32x4_t a[kRouterBatch], b[kRouterBatch];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[j] += static_cast<double>(c[j]);
+    for (int u = 0; u < kRouterBatch; ++u) {
+      if (c + u < cpp) {
+        a[u] = ld16(wp + (c + u) * 32);
+        b[u] = ld16(xp + (c + u) * 32);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRouterBatch; ++u) {
+      if (c + u < cpp) {
+        const f32x4_t f = mfma_bf16(a[u], b[u], zero);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += static_cast<double>(f[j]);
+      }
+    }
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) red[wave][lane][j] = acc[j];
@@ -55,13 +72,112 @@ __global__ __launch_bounds__(256) void k_router_bf16(const uint16_t* __restrict_
       for (int j = 0; j < 4; ++j) {
         const int e = e0 + 4 * q + j;
         if (e < E) {
-          double s = ((red[0][lane][j] + red[1][lane][j]) + red[2][lane][j]) + red[3][lane][j];
+          double s = red[0][lane][j];
+          for (int w = 1; w < nparts; ++w) s += red[w][lane][j];
           if (bias) s += static_cast<double>(bias[e]);
           logits[static_cast<size_t>(t) * E + e] = static_cast<float>(s);
         }
       }
     }
   }
+}
+
+// Large batches: each wave owns a 32-token x 32-expert tile (2 x 2 MFMA
+// tiles) and walks all parts itself, keeping a float64 part sum and a float64
+// total per output (same association as above).  grid (ceil(T/64),
+// ceil(E/64)), block 256 (waves 2 x 2 over the 64 x 64 workgroup tile).
+__global__ __launch_bounds__(256) void k_router_tiles(const uint16_t* __restrict__ x,
+                                                      const uint16_t* __restrict__ wr,
+                                                      const float* __restrict__ bias, int T, int H,
+                                                      int E, int nparts,
+                                                      float* __restrict__ logits) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, q = lane >> 4;
+  const int t0 = blockIdx.x * 64 + (wave & 1) * 32;
+  const int e0 = blockIdx.y * 64 + (wave >> 1) * 32;
+  if (t0 >= T || e0 >= E) return;
+  const int cpp = H / 32 / nparts;
+  const uint16_t* xp[2];
+  const uint16_t* wp[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    xp[i] = x + static_cast<size_t>(min(t0 + 16 * i + r, T - 1)) * H + q * 8;
+    wp[i] = wr + static_cast<size_t>(min(e0 + 16 * i + r, E - 1)) * H + q * 8;
+  }
+  double tot[2][2][4], part[2][2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) tot[a][b][j] = 0.0;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  for (int pidx = 0; pidx < nparts; ++pidx) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part[a][b][j] = 0.0;
+    const int kb = pidx * cpp * 32;
+    for (int c = 0; c < cpp; c += 4) {
+      u32x4_t wa[4][2], xb[4][2];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (c + u < cpp) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            wa[u][i] = ld16(wp[i] + kb + (c + u) * 32);
+            xb[u][i] = ld16(xp[i] + kb + (c + u) * 32);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (c + u < cpp) {
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+              const f32x4_t f = mfma_bf16(wa[u][a], xb[u][b], zero);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) part[a][b][j] += static_cast<double>(f[j]);
+            }
+        }
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tot[a][b][j] += part[a][b][j];
+  }
+  // lane holds experts e0 + 16a + 4q + j of token t0 + 16b + r
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int t = t0 + 16 * b + r;
+    if (t >= T) continue;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 16 * a + 4 * q + j;
+        if (e < E) {
+          double s = tot[a][b][j];
+          if (bias) s += static_cast<double>(bias[e]);
+          logits[static_cast<size_t>(t) * E + e] = static_cast<float>(s);
+        }
+      }
+  }
+}
+
+int router_parts(int H) {
+  const int chunks = H / 32;
+  int best = 1;
+  for (int d = 1; d <= 16; ++d)
+    if (chunks % d == 0) best = d;
+  return best;
 }
 
 // float32 router: one thread per (token, expert), products and sums in
@@ -95,15 +211,12 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   float v[16];
   uint32_t live = 0;
   if (active) {
+    const float* lt = logits + static_cast<size_t>(t) * E;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const int e = j * 64 + lane;
-      v[j] = 0.f;
-      if (e < E) {
-        v[j] = logits[static_cast<size_t>(t) * E + e];
-        live |= 1u << j;
-      }
-    }
+    for (int j = 0; j < 16; ++j) v[j] = lt[min(j * 64 + lane, E - 1)];
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+      if (j * 64 + lane < E) live |= 1u << j;
     for (int rnk = 0; rnk < k; ++rnk) {
       float bv = 0.f;
       int be = INT_MAX;
@@ -154,9 +267,16 @@ hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const
                         hipStream_t st) {
   float* lg = logits ? logits : reinterpret_cast<float*>(static_cast<char*>(ws) + pl.logits_off);
   if (s.act == MOE_DT_BF16) {
-    dim3 grid((s.T + 15) / 16, (s.E + 15) / 16);
-    hipLaunchKernelGGL(k_router_bf16, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x),
-                       static_cast<const uint16_t*>(w_router), bias, s.T, s.H, s.E, lg);
+    const int np = router_parts(s.H);
+    if (s.T <= 64) {
+      dim3 grid((s.T + 15) / 16, (s.E + 15) / 16);
+      hipLaunchKernelGGL(k_router_parts, grid, dim3(64 * np), 0, st, static_cast<const uint16_t*>(x),
+                         static_cast<const uint16_t*>(w_router), bias, s.T, s.H, s.E, np, lg);
+    } else {
+      dim3 grid((s.T + 63) / 64, (s.E + 63) / 64);
+      hipLaunchKernelGGL(k_router_tiles, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x),
+                         static_cast<const uint16_t*>(w_router), bias, s.T, s.H, s.E, np, lg);
+    }
   } else {
     const size_t n = static_cast<size_t>(s.T) * s.E;
     hipLaunchKernelGGL(k_router_f32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, st,

@@ -25,14 +25,24 @@ static size_t wrow_bytes(const moe_shape& s, int K) {
   }
 }
 
+// 16-row token groups per FFN tile, chosen from the batch size.
+static int plan_nb(const moe_shape& s) {
+  if (s.act == MOE_DT_F32 || s.T <= 16) return 1;
+  if (s.T <= 1024) return 2;
+  return 4;
+}
+
+static int64_t plan_max_tiles(const moe_shape& s) {
+  const int64_t P = static_cast<int64_t>(s.T) * s.top_k;
+  return P / (16 * plan_nb(s)) + std::min<int64_t>(s.E, P);
+}
+
 bool make_plan(const moe_shape& s, Plan* p) {
   const int64_t T = s.T, P = static_cast<int64_t>(s.T) * s.top_k;
   std::memset(p, 0, sizeof(*p));
   p->chunks = permute_single_pass(s) ? 0 : permute_chunks(s);
-  if (s.act == MOE_DT_F32 || T <= 16) p->nb = 1;
-  else if (T <= 1024) p->nb = 2;
-  else p->nb = 4;
-  p->max_tiles = static_cast<int>(P / (16 * p->nb) + std::min<int64_t>(s.E, P));
+  p->nb = plan_nb(s);
+  p->max_tiles = static_cast<int>(plan_max_tiles(s));
 
   size_t off = 0;
   p->logits_off = off;
@@ -81,7 +91,7 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 static int check_shape(const moe_shape* s) {
   if (!s) return MOE_E_NULL;
-  if (s->flags != 0) return MOE_E_FLAGS;
+  if (s->flags & ~MOE_F_TILED_WEIGHTS) return MOE_E_FLAGS;
   if (s->act != MOE_DT_F32 && s->act != MOE_DT_BF16) return MOE_E_DTYPE;
   if (s->wfmt != MOE_WF_DENSE && s->wfmt != MOE_WF_INT4_G32 && s->wfmt != MOE_WF_INT2_G32)
     return MOE_E_FORMAT;
@@ -90,9 +100,14 @@ static int check_shape(const moe_shape* s) {
   if (s->E < 1 || s->E > 1024 || s->top_k < 1 || s->top_k > s->E) return MOE_E_SHAPE;
   if (s->H <= 0 || s->H > 65536 || s->H % 128 != 0) return MOE_E_SHAPE;
   if (s->I <= 0 || s->I > 65536 || s->I % 32 != 0) return MOE_E_SHAPE;
+  if (s->flags & MOE_F_TILED_WEIGHTS) {
+    if (s->act != MOE_DT_BF16) return MOE_E_FORMAT;
+    if (s->I % 128 != 0) return MOE_E_SHAPE;
+  }
   const int64_t T = s->T;
   if (T * s->top_k >= (int64_t{1} << 31)) return MOE_E_LIMIT;
   if (T * std::max(s->E, s->H) >= (int64_t{1} << 31)) return MOE_E_LIMIT;
+  if (plan_max_tiles(*s) > 65535) return MOE_E_LIMIT;   // FFN grid y dimension
   return MOE_OK;
 }
 
@@ -324,6 +339,23 @@ int moe_ffn_down(const moe_shape* shape, const void* h, const moe_experts* exper
   if (any_alias(outs, 2, ins, 7)) return MOE_E_ALIAS;
   (void)hipGetLastError();
   return device_status(launch_down(s, pl, h, *experts, ws_tiles(pl, workspace), y, stream));
+}
+
+int moe_tile_experts(const moe_shape* shape, const moe_experts* src, const moe_experts* dst,
+                     hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const moe_shape& s = *shape;
+  if (s.flags != 0) return MOE_E_FLAGS;            // describes the row-major source
+  if (s.act != MOE_DT_BF16) return MOE_E_FORMAT;
+  if (s.I % 128 != 0) return MOE_E_SHAPE;
+  if ((st = check_experts(s, src)) || (st = check_experts(s, dst))) return st;
+  Span outs[6], ins[6];
+  expert_spans(s, *dst, outs);
+  expert_spans(s, *src, ins);
+  if (any_alias(outs, 6, ins, 6)) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  return device_status(launch_tile_experts(s, *src, *dst, stream));
 }
 
 int moe_combine(const moe_shape* shape, const void* y, const int32_t* pair_row,

@@ -54,6 +54,8 @@ hipError_t launch_down(const moe_shape& s, const Plan& pl, const void* h, const 
 hipError_t launch_ffn(const moe_shape& s, const Plan& pl, const void* x, const moe_experts& ex,
                       const int32_t* sorted_pair, const int32_t* tiles, void* h, void* y,
                       hipStream_t st);
+hipError_t launch_tile_experts(const moe_shape& s, const moe_experts& src, const moe_experts& dst,
+                               hipStream_t st);
 hipError_t launch_combine(const moe_shape& s, const void* y, const int32_t* pair_row,
                           const float* w, const void* residual, void* out, hipStream_t st);
 

@@ -10,8 +10,9 @@ from . import _abi
 class MoELayerBuffers:
     """Outputs, permutation arrays and workspace for a shape, on one device."""
 
-    def __init__(self, T, H, E, I, top_k, act="bf16", wfmt="dense", device="cuda"):
-        self.shape = _abi.make_shape(T, H, E, I, top_k, act, wfmt)
+    def __init__(self, T, H, E, I, top_k, act="bf16", wfmt="dense", device="cuda", tiled=False):
+        self.shape = _abi.make_shape(T, H, E, I, top_k, act, wfmt,
+                                     _abi.MOE_F_TILED_WEIGHTS if tiled else 0)
         self.T, self.H, self.E, self.I, self.k = T, H, E, I, top_k
         self.act = act
         dt = torch.float32 if act == "f32" else torch.bfloat16

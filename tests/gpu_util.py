@@ -62,6 +62,26 @@ class Case:
     bias64: np.ndarray | None
     ex_oracle: O.ExpertWeights
     ex_gpu: object
+    tiled_keep: dict | None = None
+    ex_gpu_tiled: object = None
+
+    def experts(self, tiled: bool):
+        return self.ex_gpu_tiled if tiled else self.ex_gpu
+
+
+def tiled_ok(cfg: MoEConfig) -> bool:
+    return cfg.act == "bf16" and cfg.I % 128 == 0
+
+
+def make_tiled(case: Case) -> None:
+    """Convert the case's row-major expert weights with moe_tile_experts."""
+    cfg, ex = case.cfg, case.li.experts
+    dst = {n: (None if t is None else torch.empty_like(t)) for n, t in ex.items()}
+    exd = M.make_experts(dst["gate"], dst["up"], dst["down"], dst["gate_scale"], dst["up_scale"],
+                         dst["down_scale"])
+    M.moe_tile_experts(M.make_shape(cfg.T, cfg.H, cfg.E, cfg.I, cfg.k, cfg.act, cfg.wfmt),
+                       case.ex_gpu, exd)
+    case.tiled_keep, case.ex_gpu_tiled = dst, exd
 
 
 def make_case(cfg: MoEConfig, layer: int = 0, x: torch.Tensor | None = None) -> Case:
@@ -77,11 +97,15 @@ def make_case(cfg: MoEConfig, layer: int = 0, x: torch.Tensor | None = None) -> 
     ex_gpu = M.make_experts(ex["gate"], ex["up"], ex["down"], ex["gate_scale"], ex["up_scale"],
                             ex["down_scale"])
     bias64 = None if li.bias is None else li.bias.double().cpu().numpy()
-    return Case(cfg, li, decode(li.x, cfg.act), decode(li.w_router, cfg.act), bias64, ex_oracle, ex_gpu)
+    case = Case(cfg, li, decode(li.x, cfg.act), decode(li.w_router, cfg.act), bias64, ex_oracle, ex_gpu)
+    if tiled_ok(cfg):
+        make_tiled(case)
+    return case
 
 
-def buffers(cfg: MoEConfig) -> M.MoELayerBuffers:
-    return M.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.I, cfg.k, cfg.act, cfg.wfmt, device=DEV)
+def buffers(cfg: MoEConfig, tiled: bool = False) -> M.MoELayerBuffers:
+    return M.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.I, cfg.k, cfg.act, cfg.wfmt, device=DEV,
+                             tiled=tiled)
 
 
 def check_routes(ids_gpu, w_gpu, logits64, ids_ref, w_ref, k):

@@ -94,7 +94,7 @@ def _route(s, b, **over):
 @pytest.mark.parametrize("field,value,code", [
     ("H", 100, 2), ("H", 0, 2), ("I", 48, 2), ("E", 2000, 2), ("top_k", 0, 2),
     ("top_k", 600, 2), ("T", -1, 2), ("T", 131073, 2), ("act", 7, 3), ("wfmt", 9, 4),
-    ("flags", 1, 10),
+    ("flags", 2, 10), ("flags", 0x80000000, 10),
 ])
 def test_route_rejects_bad_shape(field, value, code):
     b = bufs()
@@ -172,4 +172,22 @@ def test_layer_rejects_out_over_x():
                      b["ids"].addr, b["w"].addr, None, b["ws"].addr, 1 << 40, stream=0,
                      check=False)
     assert st == 6
+    assert all(v.untouched() for v in b.values())
+
+
+def test_tiled_flag_domain():
+    b = bufs()
+    assert _route(shape(flags=1, act="f32", wfmt="dense", H=256, I=128), b) == 4   # tiled needs bf16
+    assert _route(shape(flags=1, I=96), b) == 2                                      # tiled needs I % 128
+    assert all(v.untouched() for v in b.values())
+
+
+def test_tile_experts_validation():
+    b = bufs()
+    src = M.make_experts(b["g"].addr, b["u"].addr, b["d"].addr)
+    dst = M.make_experts(b["gs"].addr, b["us"].addr, b["ds"].addr)
+    assert M.moe_tile_experts(shape(flags=1), src, dst, stream=0, check=False) == 10   # source is row-major
+    assert M.moe_tile_experts(shape(), src, src, stream=0, check=False) == 6           # in place
+    assert M.moe_tile_experts(shape(I=96), src, dst, stream=0, check=False) == 2
+    assert M.moe_tile_experts(shape(), src, None, stream=0, check=False) == 1
     assert all(v.untouched() for v in b.values())

@@ -13,7 +13,7 @@ import sparse_moe_routed_amd as M
 from moe_inputs import CONFIGS, make_x
 from oracle import moe_oracle as O
 from tests.gpu_util import (DEV, buffers, check_routes, check_values, decode, i32, make_case, np_of,
-                            say, to_act_tensor)
+                            say, tiled_ok, to_act_tensor)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,6 +34,9 @@ SMALL = {
 }
 
 _cache = {}
+
+LAYOUT_CASES = [(n, lay) for n in SMALL for lay in ("row", "tiled")
+                if lay == "row" or tiled_ok(SMALL[n])]
 
 
 def get(name):
@@ -99,17 +102,41 @@ def _oracle_perm_tensors(p):
     return t, M.make_perm(*t)
 
 
-@pytest.mark.parametrize("name", list(SMALL))
-def test_grouped_ffn(name):
+@pytest.mark.parametrize("name,layout", LAYOUT_CASES)
+def test_grouped_ffn(name, layout):
     case, ref = get(name)
     cfg = case.cfg
-    buf = buffers(cfg)
+    tiled = layout == "tiled"
+    buf = buffers(cfg, tiled)
     keep, perm = _oracle_perm_tensors(ref.perm)
-    say(f"[case {name}] moe_grouped_ffn on oracle permutation")
-    buf.grouped_ffn(case.li.x, case.ex_gpu, perm=perm)
+    say(f"[case {name} {layout}] moe_grouped_ffn on oracle permutation")
+    buf.grouped_ffn(case.li.x, case.experts(tiled), perm=perm)
     sync()
     stats = check_values(decode(buf.y, cfg.act), ref.Y, cfg.act, "Y")
     say(f"[case {name}] Y {stats}")
+
+
+@pytest.mark.parametrize("name,layout", LAYOUT_CASES)
+def test_ffn_components(name, layout):
+    """moe_ffn_gate_up (SwiGLU intermediate) and moe_ffn_down separately; the
+    tile plan comes from moe_permute run on the oracle's ids."""
+    case, ref = get(name)
+    cfg = case.cfg
+    tiled = layout == "tiled"
+    buf = buffers(cfg, tiled)
+    keep, perm = _oracle_perm_tensors(ref.perm)
+    say(f"[case {name} {layout}] moe_permute + moe_ffn_gate_up")
+    buf.permute(topk_ids=i32(ref.ids))
+    buf.ffn_gate_up(case.li.x, case.experts(tiled), perm=perm)
+    sync()
+    A = O.grouped_intermediate(case.x64, ref.perm, cfg.k, case.ex_oracle)
+    hs = check_values(decode(buf.h, cfg.act), A, cfg.act, "h")
+    Ar = O.act_round(A, cfg.act)
+    say(f"[case {name} {layout}] moe_ffn_down on the oracle intermediate")
+    buf.ffn_down(case.experts(tiled), h=to_act_tensor(Ar, cfg.act))
+    sync()
+    ys = check_values(decode(buf.y, cfg.act), O.grouped_down(Ar, ref.perm, case.ex_oracle), cfg.act, "Y")
+    say(f"[case {name}] h {hs} Y {ys}")
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -129,14 +156,15 @@ def test_combine(name):
     say(f"[case {name}] combine {stats}")
 
 
-@pytest.mark.parametrize("name", list(SMALL))
-def test_layer_end_to_end(name):
+@pytest.mark.parametrize("name,layout", LAYOUT_CASES)
+def test_layer_end_to_end(name, layout):
     case, ref = get(name)
     cfg = case.cfg
-    buf = buffers(cfg)
+    tiled = layout == "tiled"
+    buf = buffers(cfg, tiled)
     res = case.li.x if cfg.residual else None
-    say(f"[case {name}] moe_layer")
-    buf.layer(case.li.x, case.li.w_router, case.li.bias, case.ex_gpu, residual=res)
+    say(f"[case {name} {layout}] moe_layer")
+    buf.layer(case.li.x, case.li.w_router, case.li.bias, case.experts(tiled), residual=res)
     sync()
     stats, same = check_routes(buf.topk_ids.cpu().numpy(), buf.topk_w.cpu().numpy().astype(np.float64),
                                ref.logits, ref.ids, ref.w, cfg.k)
@@ -171,21 +199,23 @@ def _full_layer_check(cfg, layer, n_sample, seed):
     assert np.array_equal(buf.pair_row.cpu().numpy(), ref.perm.pair_row)
     assert np.array_equal(buf.counts.cpu().numpy(), ref.perm.counts)
     keep, perm = _oracle_perm_tensors(ref.perm)
-    say(f"[full {cfg.name} layer {layer}] grouped ffn on oracle permutation")
-    buf.grouped_ffn(case.li.x, case.ex_gpu, perm=perm)
-    sync()
     rows = ref.perm.pair_row[(sample[:, None] * cfg.k + np.arange(cfg.k)).reshape(-1)]
-    yv = check_values(decode(buf.y, cfg.act)[rows], ref.Y[rows], cfg.act, "Y")
-    say(f"[full {cfg.name} layer {layer}] Y {yv}; fused layer")
     res = case.li.x if cfg.residual else None
-    buf.layer(case.li.x, case.li.w_router, case.li.bias, case.ex_gpu, residual=res)
-    sync()
-    ids = buf.topk_ids.cpu().numpy()
-    same = (ids[sample] == ref.ids[sample]).all(axis=1)
-    near = O.near_tie_tokens(ref.logits[sample], cfg.k)
-    assert (same | near).all()
-    got = decode(buf.out, cfg.act)[sample]
-    ov = check_values(got[same], ref.out[sample][same], cfg.act, "out")
+    for tiled in (False, True):
+        b2 = buffers(cfg, tiled)
+        say(f"[full {cfg.name} layer {layer} tiled={tiled}] grouped ffn on oracle permutation")
+        b2.grouped_ffn(case.li.x, case.experts(tiled), perm=perm)
+        sync()
+        yv = check_values(decode(b2.y, cfg.act)[rows], ref.Y[rows], cfg.act, "Y")
+        say(f"[full {cfg.name} layer {layer} tiled={tiled}] Y {yv}; fused layer")
+        b2.layer(case.li.x, case.li.w_router, case.li.bias, case.experts(tiled), residual=res)
+        sync()
+        ids = b2.topk_ids.cpu().numpy()
+        same = (ids[sample] == ref.ids[sample]).all(axis=1)
+        near = O.near_tie_tokens(ref.logits[sample], cfg.k)
+        assert (same | near).all()
+        got = decode(b2.out, cfg.act)[sample]
+        ov = check_values(got[same], ref.out[sample][same], cfg.act, "out")
     ua = int(ref.perm.n_active)
     say(f"[full {cfg.name} layer {layer}] out {ov}; unique experts {ua}; "
         f"repeat fraction {O.repeat_fraction(ref.ids):.3f}; max load {ref.perm.counts.max()}")
@@ -222,11 +252,11 @@ def test_stack_teacher_forced_int2():
     cases = [make_case(cfg, layer=l) for l in range(3)]
     xs = O.moe_stack(cases[0].x64, [(lambda c=c: (c.wr64, c.bias64, c.ex_oracle)) for c in cases],
                      cfg.k, cfg.act)
-    buf = buffers(cfg)
+    buf = buffers(cfg, tiled=True)
     for l, c in enumerate(cases):
         x_l = to_act_tensor(xs[l], cfg.act)
         say(f"[stack int2] layer {l}")
-        buf.layer(x_l, c.li.w_router, c.li.bias, c.ex_gpu, residual=x_l)
+        buf.layer(x_l, c.li.w_router, c.li.bias, c.ex_gpu_tiled, residual=x_l)
         sync()
         ref_r = O.moe_layer(xs[l], c.wr64, c.bias64, c.ex_oracle, cfg.k, residual=xs[l])
         stats, same = check_routes(buf.topk_ids.cpu().numpy(),
@@ -401,3 +431,35 @@ def test_t_zero_noop():
     cfg = C2.with_(T=0)
     s = M.make_shape(0, cfg.H, cfg.E, cfg.I, cfg.k)
     assert M.moe_layer(s, None, None, None, None, None, None, None, None, None, None, 0) == 0
+
+
+@pytest.mark.parametrize("wfmt", ["dense", "int4_g32", "int2_g32"])
+def test_tile_layout_bit_exact(wfmt):
+    """moe_tile_experts against the layout formula of include/moe.h,
+    evaluated with numpy reshapes."""
+    cfg = C4.with_(T=8, H=512, E=3, I=256, k=2, wfmt=wfmt)
+    case = make_case(cfg)
+    say(f"[tile layout {wfmt}]")
+    sync()
+    src, dst = case.li.experts, case.tiled_keep
+
+    def arrange(a, N, K):
+        if wfmt == "dense":                                   # [E*N][K] elements
+            v = a.reshape(-1, 16, K // 32, 4, 8).transpose(0, 2, 3, 1, 4)
+        else:
+            B = 4 if wfmt == "int4_g32" else 2                # bytes per 8 codes
+            v = a.reshape(-1, 16, K // 128, 4, 4, B).transpose(0, 2, 4, 1, 3, 5)
+        return np.ascontiguousarray(v).reshape(-1)
+
+    def arrange_scales(a, K):
+        v = a.reshape(-1, 16, K // 128, 4).transpose(0, 2, 1, 3)
+        return np.ascontiguousarray(v).reshape(-1)
+
+    for name, N, K in (("gate", cfg.I, cfg.H), ("up", cfg.I, cfg.H), ("down", cfg.H, cfg.I)):
+        a = np_of(src[name])
+        got = np_of(dst[name]).reshape(-1)
+        assert np.array_equal(got, arrange(a.reshape(a.shape[0] * a.shape[1], -1), N, K)), name
+        if wfmt != "dense":
+            sa = np_of(src[name + "_scale"])
+            sg = np_of(dst[name + "_scale"]).reshape(-1)
+            assert np.array_equal(sg, arrange_scales(sa.reshape(-1, K // 32), K)), name + " scales"

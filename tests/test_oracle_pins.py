@@ -468,3 +468,19 @@ def test_repeat_fraction_and_unique():
     ids = np.array([[0, 1], [0, 2], [3, 4]])
     assert O.unique_experts(ids) == 5
     assert O.repeat_fraction(ids) == pytest.approx(2 / 6)
+
+
+def test_grouped_stages_compose_to_ffn():
+    x, Wr, bias, ex = _tiny_layer(12, T=7)
+    ids = O.select_topk(O.router_logits(x, Wr, bias), 3)
+    perm = O.permutation(ids, Wr.shape[0])
+    A = O.grouped_intermediate(x, perm, 3, ex)
+    np.testing.assert_allclose(O.grouped_down(A, perm, ex), O.grouped_ffn(x, perm, 3, ex),
+                               rtol=1e-13, atol=1e-15)
+    # intermediate of one row against its closed form
+    r = 0
+    e = ids.reshape(-1)[perm.sorted_pair[r]]
+    t = perm.sorted_pair[r] // 3
+    wg, wu, _ = ex.expert(int(e))
+    g, u = wg @ x[t], wu @ x[t]
+    np.testing.assert_allclose(A[r], g * scipy.special.expit(g) * u, rtol=1e-13)

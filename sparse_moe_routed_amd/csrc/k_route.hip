@@ -197,69 +197,62 @@ __global__ __launch_bounds__(256) void k_router_f32(const float* __restrict__ x,
   logits[idx] = static_cast<float>(s);
 }
 
-// Exact top-k per token, one wave per token (E <= 1024: 16 logits per lane).
-// Selection uses the total order (logit descending, index ascending) on the
-// float32 logits, k rounds of a wave arg-max.  Weights: exp(l_j - l_0) / sum
-// over the selected, in float32 (the full softmax renormalized over the
-// selection).
+// Exact top-k per token, one wave per token; lane l holds the logits of
+// experts l, 64 + l, ... (NV slots, E <= 64 NV).  Each of the k rounds takes
+// the wave maximum m of the remaining logits, then the smallest expert index
+// whose logit equals m -- the total order (logit descending, index
+// ascending) -- with DPP row reductions and readlanes (no LDS round trips).
+// -0.0 and +0.0 compare equal.  Weights: exp(l_j - l_0) / sum over the
+// selected, in float32 (the full softmax renormalized over the selection).
+template <int NV>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
                                               int32_t* __restrict__ ids, float* __restrict__ w) {
   __shared__ float sel[4][1024];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
-  const bool active = t < T;
-  float v[16];
+  if (t >= T) return;   // whole wave leaves; no workgroup barrier below
+  const float* lt = logits + static_cast<size_t>(t) * E;
+  float v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = lt[min(j * 64 + lane, E - 1)];
   uint32_t live = 0;
-  if (active) {
-    const float* lt = logits + static_cast<size_t>(t) * E;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = lt[min(j * 64 + lane, E - 1)];
+  for (int j = 0; j < NV; ++j)
+    if (j * 64 + lane < E) live |= 1u << j;
+  for (int rnk = 0; rnk < k; ++rnk) {
+    float lm = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if (j * 64 + lane < E) live |= 1u << j;
-    for (int rnk = 0; rnk < k; ++rnk) {
-      float bv = 0.f;
-      int be = INT_MAX;
+    for (int j = 0; j < NV; ++j)
+      if ((live >> j) & 1u) lm = fmaxf(lm, v[j]);
+    const float m = wave_max_f32(lm);
+    uint32_t li = 0xffffffffu;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        if ((live >> j) & 1u) {
-          const int e = j * 64 + lane;
-          if (be == INT_MAX || v[j] > bv || (v[j] == bv && e < be)) {
-            bv = v[j];
-            be = e;
-          }
-        }
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, kWave);
-        const int oe = __shfl_xor(be, off, kWave);
-        const bool take = oe != INT_MAX && (be == INT_MAX || ov > bv || (ov == bv && oe < be));
-        if (take) {
-          bv = ov;
-          be = oe;
-        }
-      }
-      if ((be & 63) == lane) live &= ~(1u << (be >> 6));
-      if (lane == 0) {
-        ids[static_cast<size_t>(t) * k + rnk] = be;
-        sel[wave][rnk] = bv;
-      }
+    for (int j = NV - 1; j >= 0; --j)
+      if (((live >> j) & 1u) && v[j] == m) li = static_cast<uint32_t>(j * 64 + lane);
+    const uint32_t e = wave_min_u32(li);
+    if (static_cast<int>(e & 63u) == lane) live &= ~(1u << (e >> 6));
+    if (lane == 0) {
+      ids[static_cast<size_t>(t) * k + rnk] = static_cast<int32_t>(e);
+      sel[wave][rnk] = m;
     }
   }
-  __syncthreads();
-  if (active) {
-    const float m0 = sel[wave][0];
-    float sum = 0.f;
-    for (int rnk = lane; rnk < k; rnk += 64) {
-      const float ex = expf(sel[wave][rnk] - m0);
-      sel[wave][rnk] = ex;
-      sum += ex;
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, kWave);
-    for (int rnk = lane; rnk < k; rnk += 64) w[static_cast<size_t>(t) * k + rnk] = sel[wave][rnk] / sum;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const float m0 = sel[wave][0];
+  float part = 0.f;
+  for (int rnk = lane; rnk < k; rnk += 64) {
+    const float ex = expf(sel[wave][rnk] - m0);
+    sel[wave][rnk] = ex;
+    part += ex;
   }
+  const float sum = wave_sum_f32(part);
+  for (int rnk = lane; rnk < k; rnk += 64) w[static_cast<size_t>(t) * k + rnk] = sel[wave][rnk] / sum;
+}
+
+template <int NV>
+static void launch_topk(const moe_shape& s, const float* lg, int32_t* ids, float* w, hipStream_t st) {
+  hipLaunchKernelGGL((k_topk<NV>), dim3((s.T + 3) / 4), dim3(256), 0, st, lg, s.T, s.E, s.top_k, ids, w);
 }
 
 hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const void* w_router,
@@ -283,7 +276,12 @@ hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const
                        static_cast<const float*>(x), static_cast<const float*>(w_router), bias, s.T,
                        s.H, s.E, lg);
   }
-  hipLaunchKernelGGL(k_topk, dim3((s.T + 3) / 4), dim3(256), 0, st, lg, s.T, s.E, s.top_k, ids, w);
+  const int nv = (s.E + 63) / 64;
+  if (nv <= 1) launch_topk<1>(s, lg, ids, w, st);
+  else if (nv <= 2) launch_topk<2>(s, lg, ids, w, st);
+  else if (nv <= 4) launch_topk<4>(s, lg, ids, w, st);
+  else if (nv <= 8) launch_topk<8>(s, lg, ids, w, st);
+  else launch_topk<16>(s, lg, ids, w, st);
   return hipGetLastError();
 }
 

@@ -89,4 +89,53 @@ __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);
 }
 
+// DPP lane permutations within 16-lane rows (few-cycle latency, no LDS).
+constexpr int kDppXor1 = 0xB1;        // quad_perm(1,0,3,2)
+constexpr int kDppXor2 = 0x4E;        // quad_perm(2,3,0,1)
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within each 8-lane half row
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within each row
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), CTRL, 0xF, 0xF, false));
+}
+
+// Maximum of a float over the wave, returned to every lane (wave-uniform).
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppHalfMirror>(__float_as_uint(v))));
+  v = fmaxf(v, __uint_as_float(dpp_u32<kDppMirror>(__float_as_uint(v))));
+  const float r0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
+  const float r1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 16));
+  const float r2 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 32));
+  const float r3 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Minimum of an unsigned value over the wave (wave-uniform result).
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<kDppXor1>(v));
+  v = min(v, dpp_u32<kDppXor2>(v));
+  v = min(v, dpp_u32<kDppHalfMirror>(v));
+  v = min(v, dpp_u32<kDppMirror>(v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return min(min(r0, r1), min(r2, r3));
+}
+
+// Sum of a float over the wave in a fixed association (wave-uniform result).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppHalfMirror>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppMirror>(__float_as_uint(v)));
+  const float r0 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 0));
+  const float r1 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 16));
+  const float r2 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 32));
+  const float r3 = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 }  // namespace moe

@@ -121,11 +121,12 @@ typedef struct {
  * with nb < N/16, r < 16, q < 4, j < 8:
  *   bf16: element W[16nb + r][32ks + 8q + j] at element index
  *         ((nb*(K/32) + ks)*64 + 16q + r)*8 + j           (ks < K/32);
- *   int4/int2: the 8 codes W[16nb + r][128kb + 32s + 8q + j] (j = 0..7, in
- *         the row-major little-endian packing of 8 codes: 4 bytes for int4,
- *         2 bytes for int2) at byte offset
- *         ((nb*(K/128) + kb)*64 + 16q + r)*B + s*(B/4)    (kb < K/128, s < 4,
- *         B = 16 for int4, 8 for int2);
+ *   int4/int2: the 8 codes c_j = W[16nb + r][128kb + 32s + 8q + j] (j = 0..7)
+ *         at byte offset ((nb*(K/128) + kb)*64 + 16q + r)*B + s*(B/4)
+ *         (kb < K/128, s < 4, B = 16 for int4, 8 for int2), packed as:
+ *         int2: 2 bytes, c_j at bits 2j..2j+1 (the row-major packing);
+ *         int4: 4 bytes, c_2m at nibble m and c_2m+1 at nibble m+4 (m < 4),
+ *         so that one mask extracts a (c_2m, c_2m+1) pair;
  *   scales: scale[16nb + r][4kb + s] at fp16 index ((nb*(K/128) + kb)*16 + r)*4 + s.
  * Requirements: bf16 activations; I % 128 == 0 (MOE_E_SHAPE otherwise). */
 

@@ -363,10 +363,10 @@ __device__ __forceinline__ u32x4_t tdecode(const TRaw<WF>& t, int s) {
   if constexpr (WF == WF_BF16) {
     return t.v[s];
   } else if constexpr (WF == WF_INT4) {
-    return dequant_int4x8(t.v[0][s]);
+    return dequant_int4_offset(t.v[0][s]);
   } else {
     const uint32_t d = t.v[0][s >> 1];
-    return dequant_int2x8((s & 1) ? (d >> 16) : (d & 0xffffu));
+    return dequant_int2_offset((s & 1) ? (d >> 16) : d);
   }
 }
 
@@ -374,18 +374,29 @@ __device__ __forceinline__ Scales<4> tscales(const uint16_t* sc, size_t nb, int 
   return load_scales<4>(sc + ((nb * static_cast<size_t>(K / 128) + kb) * 16 + r) * 4, 0);
 }
 
-// gate/up + SwiGLU on tiled weights.  A workgroup has 4 waves = (4/KSPLIT)
-// row groups x KSPLIT k parts; each row group is 32 intermediate rows of gate
-// and of up; the k parts of a row group are added in LDS in part order.
-// grid (I / (32 * 4 / KSPLIT), max_tiles), block 256.
-template <int WF, int NB, int KSPLIT>
+template <int WF>
+__device__ __forceinline__ u32x4_t neg_offset_fragment() {
+  const uint32_t c = (WF == WF_INT4) ? kNegOffset4 : kNegOffset2;
+  return u32x4_t{c, c, c, c};
+}
+
+// gate/up + SwiGLU on tiled weights.  A wave owns MB 16-row blocks of gate
+// and of up (16 MB intermediate rows); a workgroup has 4 waves = (4/KSPLIT)
+// row groups x KSPLIT k parts, and the k parts of a row group are added in
+// LDS in part order (two row blocks at a time).  Low-bit codes enter the MFMA
+// as 128 + offset + q; the C operand carries -offset * sum(x) (one MFMA of x
+// against a constant fragment per 32-k chunk, shared by all the wave's rows),
+// so each group partial is sum(q x) before its fp16 scale is applied.
+// grid (I / (16 * MB * 4 / KSPLIT), max_tiles), block 256.
+template <int WF, int NB, int KSPLIT, int MB, bool PF>
 __global__ __launch_bounds__(256) void k_gateup_t(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
     const uint16_t* __restrict__ sg, const uint16_t* __restrict__ su,
     const int32_t* __restrict__ tiles, int max_tiles, const int32_t* __restrict__ sorted_pair,
     int k, int H, int I, int P, uint16_t* __restrict__ h) {
   constexpr int RG = 4 / KSPLIT;
-  __shared__ f32x4_t red[KSPLIT > 1 ? 4 : 1][2][2][NB][64];
+  constexpr int RB = MB < 2 ? MB : 2;              // row blocks reduced per LDS pass
+  __shared__ f32x4_t red[KSPLIT > 1 ? 4 : 1][RB][2][NB][64];
   const int n_tiles = tiles[3 * max_tiles];
   if (static_cast<int>(blockIdx.y) >= n_tiles) return;
   const Tile tl = read_tile(tiles, blockIdx.y);
@@ -393,7 +404,7 @@ __global__ __launch_bounds__(256) void k_gateup_t(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
   const int kp = wave % KSPLIT, rg = wave / KSPLIT;
-  const int i0 = (blockIdx.x * RG + rg) * 32;
+  const int i0 = (blockIdx.x * RG + rg) * 16 * MB;
   const int units = H / 128 / KSPLIT;
   const int ub = kp * units;
   const size_t nb0 = (static_cast<size_t>(tl.e) * I + i0) / 16;
@@ -407,49 +418,59 @@ __global__ __launch_bounds__(256) void k_gateup_t(
     px[b] = x + static_cast<size_t>(p / k) * H + q * 8;
   }
 
-  f32x4_t acc[2][2][NB];
+  f32x4_t acc[MB][2][NB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int gu = 0; gu < 2; ++gu)
 #pragma unroll
       for (int b = 0; b < NB; ++b) acc[mb][gu][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int u = ub; u < ub + units; ++u) {
-    Scales<4> sc[2][2];
+  struct Stage {
+    Scales<4> sc[MB][2];
+    TRaw<WF> raw[MB][2];
+    u32x4_t xa[4][NB];
+  };
+  auto load = [&](Stage& S, int u) {
     if constexpr (WF != WF_BF16) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        sc[mb][0] = tscales(sg, nb0 + mb, H, u, r);
-        sc[mb][1] = tscales(su, nb0 + mb, H, u, r);
+      for (int mb = 0; mb < MB; ++mb) {
+        S.sc[mb][0] = tscales(sg, nb0 + mb, H, u, r);
+        S.sc[mb][1] = tscales(su, nb0 + mb, H, u, r);
       }
     }
-    TRaw<WF> raw[2][2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      raw[mb][0] = tload<WF>(wg, nb0 + mb, H, u, lane);
-      raw[mb][1] = tload<WF>(wu, nb0 + mb, H, u, lane);
+    for (int mb = 0; mb < MB; ++mb) {
+      S.raw[mb][0] = tload<WF>(wg, nb0 + mb, H, u, lane);
+      S.raw[mb][1] = tload<WF>(wu, nb0 + mb, H, u, lane);
     }
-    u32x4_t xa[4][NB];
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) xa[st][b] = ld16(px[b] + 128 * u + 32 * st);
+      for (int b = 0; b < NB; ++b) S.xa[st][b] = ld16(px[b] + 128 * u + 32 * st);
+  };
+  auto compute = [&](const Stage& S) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
+      f32x4_t corr[NB];
+      if constexpr (WF != WF_BF16) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
+        for (int b = 0; b < NB; ++b)
+          corr[b] = mfma_bf16(S.xa[st][b], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int gu = 0; gu < 2; ++gu) {
-          const u32x4_t wv = tdecode<WF>(raw[mb][gu], st);
+          const u32x4_t wv = tdecode<WF>(S.raw[mb][gu], st);
           if constexpr (WF == WF_BF16) {
 #pragma unroll
-            for (int b = 0; b < NB; ++b) acc[mb][gu][b] = mfma_bf16(xa[st][b], wv, acc[mb][gu][b]);
+            for (int b = 0; b < NB; ++b) acc[mb][gu][b] = mfma_bf16(S.xa[st][b], wv, acc[mb][gu][b]);
           } else {
-            const float sv = fp16_to_f32(sc[mb][gu].s[st]);
+            const float sv = fp16_to_f32(S.sc[mb][gu].s[st]);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-              const f32x4_t pp = mfma_bf16(xa[st][b], wv, f32x4_t{0.f, 0.f, 0.f, 0.f});
+              const f32x4_t pp = mfma_bf16(S.xa[st][b], wv, corr[b]);
 #pragma unroll
               for (int j = 0; j < 4; ++j) acc[mb][gu][b][j] = fmaf(sv, pp[j], acc[mb][gu][b][j]);
             }
@@ -457,35 +478,60 @@ __global__ __launch_bounds__(256) void k_gateup_t(
         }
       }
     }
+  };
+  const int ue = ub + units;
+  if constexpr (PF) {
+    // two register stages: the next unit's loads are in flight while the
+    // current unit is computed
+    Stage s0, s1;
+    load(s0, ub);
+    for (int u = ub; u < ue; u += 2) {
+      if (u + 1 < ue) load(s1, u + 1);
+      compute(s0);
+      if (u + 1 < ue) {
+        if (u + 2 < ue) load(s0, u + 2);
+        compute(s1);
+      }
+    }
+  } else {
+    for (int u = ub; u < ue; ++u) {
+      Stage s0;
+      load(s0, u);
+      compute(s0);
+    }
   }
 
   if constexpr (KSPLIT > 1) {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int m0 = 0; m0 < MB; m0 += RB) {
+      if (m0 > 0) __syncthreads();
 #pragma unroll
-      for (int gu = 0; gu < 2; ++gu)
+      for (int mm = 0; mm < RB; ++mm)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) red[wave][mb][gu][b][lane] = acc[mb][gu][b];
-    __syncthreads();
-    for (int idx = wave; idx < RG * 2 * NB; idx += 4) {
-      const int g_ = idx / (2 * NB), rem = idx % (2 * NB);
-      const int mb = rem & 1, b = rem >> 1;
-      f32x4_t G = red[g_ * KSPLIT][mb][0][b][lane], U_ = red[g_ * KSPLIT][mb][1][b][lane];
+        for (int gu = 0; gu < 2; ++gu)
 #pragma unroll
-      for (int w = 1; w < KSPLIT; ++w) {
-        G += red[g_ * KSPLIT + w][mb][0][b][lane];
-        U_ += red[g_ * KSPLIT + w][mb][1][b][lane];
-      }
-      const int i = (blockIdx.x * RG + g_) * 32 + mb * 16 + r;
+          for (int b = 0; b < NB; ++b) red[wave][mm][gu][b][lane] = acc[m0 + mm][gu][b];
+      __syncthreads();
+      for (int idx = wave; idx < RG * RB * NB; idx += 4) {
+        const int g_ = idx / (RB * NB), rem = idx % (RB * NB);
+        const int mm = rem % RB, b = rem / RB;
+        f32x4_t G = red[g_ * KSPLIT][mm][0][b][lane], U_ = red[g_ * KSPLIT][mm][1][b][lane];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rr = b * 16 + 4 * q + j;
-        if (rr < tl.rows) h[static_cast<size_t>(tl.row0 + rr) * I + i] = f32_to_bf16(silu(G[j]) * U_[j]);
+        for (int w = 1; w < KSPLIT; ++w) {
+          G += red[g_ * KSPLIT + w][mm][0][b][lane];
+          U_ += red[g_ * KSPLIT + w][mm][1][b][lane];
+        }
+        const int i = (blockIdx.x * RG + g_) * 16 * MB + (m0 + mm) * 16 + r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rr = b * 16 + 4 * q + j;
+          if (rr < tl.rows) h[static_cast<size_t>(tl.row0 + rr) * I + i] = f32_to_bf16(silu(G[j]) * U_[j]);
+        }
       }
     }
   } else {
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {
       const int i = i0 + mb * 16 + r;
 #pragma unroll
       for (int b = 0; b < NB; ++b)
@@ -500,9 +546,9 @@ __global__ __launch_bounds__(256) void k_gateup_t(
   }
 }
 
-// down on tiled weights: 32 output features per wave, 128 per workgroup,
-// full K = I.  grid (H / 128, max_tiles), block 256.
-template <int WF, int NB>
+// down on tiled weights: MB 16-row blocks of output features per wave,
+// 64 MB per workgroup, full K = I.  grid (H / (64 MB), max_tiles), block 256.
+template <int WF, int NB, int MB, bool PF>
 __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
                                                 const uint8_t* __restrict__ wd,
                                                 const uint16_t* __restrict__ sd,
@@ -514,56 +560,84 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
   if (tl.rows <= 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
-  const int n0 = (blockIdx.x * 4 + wave) * 32;
+  const int n0 = (blockIdx.x * 4 + wave) * 16 * MB;
   const size_t nb0 = (static_cast<size_t>(tl.e) * H + n0) / 16;
   const uint16_t* ph[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
     ph[b] = h + static_cast<size_t>(tl.row0 + min(b * 16 + r, tl.rows - 1)) * I + q * 8;
 
-  f32x4_t acc[2][NB];
+  f32x4_t acc[MB][NB];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
     for (int b = 0; b < NB; ++b) acc[mb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int units = I / 128;
-  for (int u = 0; u < units; ++u) {
-    Scales<4> sc[2];
+  struct Stage {
+    Scales<4> sc[MB];
+    TRaw<WF> raw[MB];
+    u32x4_t ha[4][NB];
+  };
+  auto load = [&](Stage& S, int u) {
     if constexpr (WF != WF_BF16) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) sc[mb] = tscales(sd, nb0 + mb, I, u, r);
+      for (int mb = 0; mb < MB; ++mb) S.sc[mb] = tscales(sd, nb0 + mb, I, u, r);
     }
-    TRaw<WF> raw[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) raw[mb] = tload<WF>(wd, nb0 + mb, I, u, lane);
-    u32x4_t ha[4][NB];
+    for (int mb = 0; mb < MB; ++mb) S.raw[mb] = tload<WF>(wd, nb0 + mb, I, u, lane);
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) ha[st][b] = ld16(ph[b] + 128 * u + 32 * st);
+      for (int b = 0; b < NB; ++b) S.ha[st][b] = ld16(ph[b] + 128 * u + 32 * st);
+  };
+  auto compute = [&](const Stage& S) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
+      f32x4_t corr[NB];
+      if constexpr (WF != WF_BF16) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const u32x4_t wv = tdecode<WF>(raw[mb], st);
+        for (int b = 0; b < NB; ++b)
+          corr[b] = mfma_bf16(S.ha[st][b], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const u32x4_t wv = tdecode<WF>(S.raw[mb], st);
         if constexpr (WF == WF_BF16) {
 #pragma unroll
-          for (int b = 0; b < NB; ++b) acc[mb][b] = mfma_bf16(ha[st][b], wv, acc[mb][b]);
+          for (int b = 0; b < NB; ++b) acc[mb][b] = mfma_bf16(S.ha[st][b], wv, acc[mb][b]);
         } else {
-          const float sv = fp16_to_f32(sc[mb].s[st]);
+          const float sv = fp16_to_f32(S.sc[mb].s[st]);
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
-            const f32x4_t pp = mfma_bf16(ha[st][b], wv, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            const f32x4_t pp = mfma_bf16(S.ha[st][b], wv, corr[b]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[mb][b][j] = fmaf(sv, pp[j], acc[mb][b][j]);
           }
         }
       }
     }
+  };
+  const int units = I / 128;
+  if constexpr (PF) {
+    Stage s0, s1;
+    load(s0, 0);
+    for (int u = 0; u < units; u += 2) {
+      if (u + 1 < units) load(s1, u + 1);
+      compute(s0);
+      if (u + 1 < units) {
+        if (u + 2 < units) load(s0, u + 2);
+        compute(s1);
+      }
+    }
+  } else {
+    for (int u = 0; u < units; ++u) {
+      Stage s0;
+      load(s0, u);
+      compute(s0);
+    }
   }
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < MB; ++mb) {
     const int n = n0 + mb * 16 + r;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
@@ -656,30 +730,67 @@ static void launch_down_wf(const moe_shape& s, const Plan& pl, const void* h,
                        s.I, static_cast<uint16_t*>(y));
 }
 
+// Rows per wave (16 MB) for the tiled kernels: bf16 keeps 32 rows (the raw
+// fragments are 64 B per lane per row block); low-bit formats take more rows
+// so that every token fragment feeds more MFMAs and each wave streams more
+// bytes.  `rows` is the row count one workgroup covers for MB = 1.
+// Two-stage register prefetch across k units.  Measured on MI355X it loses
+// for every format at the row counts below (the second stage costs the
+// registers that more rows per wave -- fewer token loads per weight byte --
+// put to better use), so it is off; the path stays for other shapes.
+template <int WF>
+constexpr bool kPrefetch = false;
+
+template <int WF, int NB>
+constexpr int tiled_mb_max() {
+  // registers: accumulators grow with MB * NB and the prefetched stage with
+  // MB; these keep every launched variant within the 512-register wave
+  // budget without spills
+  return WF == WF_BF16 ? 2 : (WF == WF_INT4 ? (NB >= 4 ? 2 : 4) : (8 / NB));
+}
+
+template <int WF, int NB>
+static int tiled_mb(int N, int rows_per_mb1) {
+  for (int mb = tiled_mb_max<WF, NB>(); mb >= 1; mb >>= 1)
+    if (N % (rows_per_mb1 * mb) == 0) return mb;
+  return 1;
+}
+
+template <int WF, int NB, int KSPLIT, int MB>
+static void gateup_tiled_launch(const moe_shape& s, const Plan& pl, const void* x,
+                                const moe_experts& ex, const int32_t* sorted_pair,
+                                const int32_t* tiles, void* h, hipStream_t st) {
+  const dim3 grid(s.I / (16 * MB * (4 / KSPLIT)), pl.max_tiles);
+  hipLaunchKernelGGL((k_gateup_t<WF, NB, KSPLIT, MB, kPrefetch<WF>>), grid, dim3(256), 0, st,
+                     static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(ex.gate),
+                     static_cast<const uint8_t*>(ex.up), ex.gate_scale, ex.up_scale, tiles,
+                     pl.max_tiles, sorted_pair, s.top_k, s.H, s.I, s.T * s.top_k,
+                     static_cast<uint16_t*>(h));
+}
+
+template <int WF, int NB, int KSPLIT>
+static void gateup_tiled_mb(const moe_shape& s, const Plan& pl, const void* x,
+                            const moe_experts& ex, const int32_t* sp, const int32_t* tiles,
+                            void* h, hipStream_t st) {
+  constexpr int M = tiled_mb_max<WF, NB>();
+  switch (tiled_mb<WF, NB>(s.I, 16 * (4 / KSPLIT))) {
+    case M: gateup_tiled_launch<WF, NB, KSPLIT, M>(s, pl, x, ex, sp, tiles, h, st); break;
+    case (M > 1 ? M / 2 : 0):
+      gateup_tiled_launch<WF, NB, KSPLIT, (M > 1 ? M / 2 : 1)>(s, pl, x, ex, sp, tiles, h, st); break;
+    default: gateup_tiled_launch<WF, NB, KSPLIT, 1>(s, pl, x, ex, sp, tiles, h, st); break;
+  }
+}
+
 template <int WF, int NB>
 static void launch_gateup_tiled(const moe_shape& s, const Plan& pl, const void* x,
                                 const moe_experts& ex, const int32_t* sorted_pair,
                                 const int32_t* tiles, void* h, hipStream_t st) {
-  const int P = s.T * s.top_k;
-  const uint16_t* xb = static_cast<const uint16_t*>(x);
-  uint16_t* hb = static_cast<uint16_t*>(h);
-  const uint8_t* g8 = static_cast<const uint8_t*>(ex.gate);
-  const uint8_t* u8 = static_cast<const uint8_t*>(ex.up);
   // k split across the waves of a workgroup: 4 parts for small batches when
   // H allows (more workgroups stream at once), fewer otherwise
   const int ksplit = (NB <= 2 && s.H % 512 == 0) ? 4 : ((NB <= 2 && s.H % 256 == 0) ? 2 : 1);
-  if (ksplit == 4)
-    hipLaunchKernelGGL((k_gateup_t<WF, NB, 4>), dim3(s.I / 32, pl.max_tiles), dim3(256), 0, st, xb,
-                       g8, u8, ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair,
-                       s.top_k, s.H, s.I, P, hb);
-  else if (ksplit == 2)
-    hipLaunchKernelGGL((k_gateup_t<WF, NB, 2>), dim3(s.I / 64, pl.max_tiles), dim3(256), 0, st, xb,
-                       g8, u8, ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair,
-                       s.top_k, s.H, s.I, P, hb);
-  else
-    hipLaunchKernelGGL((k_gateup_t<WF, NB, 1>), dim3(s.I / 128, pl.max_tiles), dim3(256), 0, st, xb,
-                       g8, u8, ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair,
-                       s.top_k, s.H, s.I, P, hb);
+  if (ksplit == 4) gateup_tiled_mb<WF, NB, 4>(s, pl, x, ex, sorted_pair, tiles, h, st);
+  else if (ksplit == 2) gateup_tiled_mb<WF, NB, 2>(s, pl, x, ex, sorted_pair, tiles, h, st);
+  else gateup_tiled_mb<WF, NB, 1>(s, pl, x, ex, sorted_pair, tiles, h, st);
 }
 
 template <int WF>
@@ -700,13 +811,25 @@ static void gateup_nb(const moe_shape& s, const Plan& pl, const void* x, const m
   }
 }
 
+template <int WF, int NB, int MB>
+static void down_tiled_launch(const moe_shape& s, const Plan& pl, const void* h,
+                              const moe_experts& ex, const int32_t* tiles, void* y,
+                              hipStream_t st) {
+  hipLaunchKernelGGL((k_down_t<WF, NB, MB, kPrefetch<WF>>), dim3(s.H / (64 * MB), pl.max_tiles), dim3(256), 0, st,
+                     static_cast<const uint16_t*>(h), static_cast<const uint8_t*>(ex.down),
+                     ex.down_scale, tiles, pl.max_tiles, s.H, s.I, static_cast<uint16_t*>(y));
+}
+
 template <int WF, int NB>
 static void launch_down_tiled(const moe_shape& s, const Plan& pl, const void* h,
                               const moe_experts& ex, const int32_t* tiles, void* y,
                               hipStream_t st) {
-  hipLaunchKernelGGL((k_down_t<WF, NB>), dim3(s.H / 128, pl.max_tiles), dim3(256), 0, st,
-                     static_cast<const uint16_t*>(h), static_cast<const uint8_t*>(ex.down),
-                     ex.down_scale, tiles, pl.max_tiles, s.H, s.I, static_cast<uint16_t*>(y));
+  constexpr int M = tiled_mb_max<WF, NB>();
+  switch (tiled_mb<WF, NB>(s.H, 64)) {
+    case M: down_tiled_launch<WF, NB, M>(s, pl, h, ex, tiles, y, st); break;
+    case (M > 1 ? M / 2 : 0): down_tiled_launch<WF, NB, (M > 1 ? M / 2 : 1)>(s, pl, h, ex, tiles, y, st); break;
+    default: down_tiled_launch<WF, NB, 1>(s, pl, h, ex, tiles, y, st); break;
+  }
 }
 
 template <int WF>

@@ -39,7 +39,15 @@ __global__ __launch_bounds__(256) void k_tile_codes(const uint8_t* __restrict__ 
   for (int s = 0; s < 4; ++s) {
     const size_t b = row + (kb * 128 + s * 32 + q * 8) * BITS / 8;
     if constexpr (BITS == 4) {
-      *reinterpret_cast<uint32_t*>(o + s * 4) = *reinterpret_cast<const uint32_t*>(src + b);
+      // natural nibble order c0..c7 -> tiled order (nibble m: c_2m, nibble m+4: c_2m+1)
+      const uint32_t v = *reinterpret_cast<const uint32_t*>(src + b);
+      uint32_t t = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        t |= ((v >> (8 * m)) & 0xFu) << (4 * m);
+        t |= ((v >> (8 * m + 4)) & 0xFu) << (4 * (m + 4));
+      }
+      *reinterpret_cast<uint32_t*>(o + s * 4) = t;
     } else {
       *reinterpret_cast<uint16_t*>(o + s * 2) = *reinterpret_cast<const uint16_t*>(src + b);
     }

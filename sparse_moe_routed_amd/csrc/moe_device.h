@@ -84,6 +84,40 @@ __device__ __forceinline__ u32x4_t dequant_int2x8(uint32_t w16) {
   return r;
 }
 
+// Offset ("magic") dequantization for the tiled low-bit layouts.  A code q is
+// turned into the exact bf16 integer 128 + (q + bias) by OR-ing its offset
+// binary value into the mantissa of 128.0 (bf16 0x4300): bias 8 for int4
+// (values 136 + q) and 2 for int2 (130 + q); the constant part is removed by
+// an MFMA against a fragment of -136 / -130 (kNegOffset*), which is exact in
+// bf16.  One AND-OR per pair of codes.
+constexpr uint32_t kNegOffset4 = 0xC308C308u;   // bf16 pair (-136, -136)
+constexpr uint32_t kNegOffset2 = 0xC302C302u;   // bf16 pair (-130, -130)
+
+// 8 int4 codes in the tiled nibble order (nibble m: code 2m, nibble m+4:
+// code 2m+1) -> 4 bf16 pairs (136 + q_2m, 136 + q_2m+1), m = 0..3.
+__device__ __forceinline__ u32x4_t dequant_int4_offset(uint32_t w) {
+  const uint32_t t = w ^ 0x88888888u;
+  u32x4_t r;
+  r[0] = (t & 0x000F000Fu) | 0x43004300u;
+  r[1] = ((t >> 4) & 0x000F000Fu) | 0x43004300u;
+  r[2] = ((t >> 8) & 0x000F000Fu) | 0x43004300u;
+  r[3] = ((t >> 12) & 0x000F000Fu) | 0x43004300u;
+  return r;
+}
+
+// 8 int2 codes (natural order, 2 bits each, low bits first) -> 4 bf16 pairs
+// (130 + q_2m, 130 + q_2m+1).
+__device__ __forceinline__ u32x4_t dequant_int2_offset(uint32_t w16) {
+  const uint32_t t = (w16 & 0xFFFFu) ^ 0xAAAAu;
+  const uint32_t u = t | (t << 14);
+  u32x4_t r;
+  r[0] = (u & 0x00030003u) | 0x43004300u;
+  r[1] = ((u >> 4) & 0x00030003u) | 0x43004300u;
+  r[2] = ((u >> 8) & 0x00030003u) | 0x43004300u;
+  r[3] = ((u >> 12) & 0x00030003u) | 0x43004300u;
+  return r;
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);

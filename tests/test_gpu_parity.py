@@ -443,13 +443,23 @@ def test_tile_layout_bit_exact(wfmt):
     sync()
     src, dst = case.li.experts, case.tiled_keep
 
+    def int4_split_nibbles(v):
+        """natural nibble order c0..c7 of each 4-byte piece -> c_2m at nibble m,
+        c_2m+1 at nibble m+4"""
+        d = np.ascontiguousarray(v).reshape(-1, 4).copy().view(np.uint32).reshape(-1).astype(np.uint64)
+        out = np.zeros_like(d)
+        for m in range(4):
+            out |= ((d >> (8 * m)) & 0xF) << (4 * m)
+            out |= ((d >> (8 * m + 4)) & 0xF) << (4 * (m + 4))
+        return out.astype(np.uint32).view(np.uint8)
+
     def arrange(a, N, K):
         if wfmt == "dense":                                   # [E*N][K] elements
             v = a.reshape(-1, 16, K // 32, 4, 8).transpose(0, 2, 3, 1, 4)
-        else:
-            B = 4 if wfmt == "int4_g32" else 2                # bytes per 8 codes
-            v = a.reshape(-1, 16, K // 128, 4, 4, B).transpose(0, 2, 4, 1, 3, 5)
-        return np.ascontiguousarray(v).reshape(-1)
+            return np.ascontiguousarray(v).reshape(-1)
+        B = 4 if wfmt == "int4_g32" else 2                    # bytes per 8 codes
+        v = np.ascontiguousarray(a.reshape(-1, 16, K // 128, 4, 4, B).transpose(0, 2, 4, 1, 3, 5))
+        return int4_split_nibbles(v) if wfmt == "int4_g32" else v.reshape(-1)
 
     def arrange_scales(a, K):
         v = a.reshape(-1, 16, K // 128, 4).transpose(0, 2, 1, 3)

@@ -687,6 +687,210 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large batches: token rows staged through LDS.
+//
+// With 64-row token tiles every wave of a workgroup needs the same token
+// fragments; loading them per wave makes the per-CU load path (not HBM) the
+// limit.  Here the workgroup copies each 64 x 128 token unit into LDS once,
+// with full 256-byte row segments per load, already in MFMA fragment order,
+// and the waves read their A fragments from LDS; weights still stream from
+// HBM straight into registers.  Two LDS buffers: the next unit is loaded
+// into registers while the current one is multiplied, then stored.
+
+// gate/up + SwiGLU, KSPLIT = 1: each wave owns MB 16-row blocks of gate and
+// of up (64 MB rows per workgroup) over the full K = H.  1-D grid over
+// (tile, slice) items, block 256.
+template <int WF, int NB, int MB>
+__global__ __launch_bounds__(256) void k_gateup_x(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
+    const uint16_t* __restrict__ sg, const uint16_t* __restrict__ su,
+    const int32_t* __restrict__ tiles, int max_tiles, const int32_t* __restrict__ sorted_pair,
+    int k, int H, int I, int P, uint16_t* __restrict__ h, int band, int xcd) {
+  __shared__ __align__(16) char xs[2][NB * 4096];
+  int ti, sl;
+  if (!tile_item(tiles[3 * max_tiles], I / (64 * MB), band, xcd != 0, ti, sl)) return;
+  const Tile tl = read_tile(tiles, ti);
+  if (tl.rows <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, q = lane >> 4;
+  const int i0 = (sl * 4 + wave) * 16 * MB;
+  const int units = H / 128;
+  const size_t nb0 = (static_cast<size_t>(tl.e) * I + i0) / 16;
+
+  XUnit<NB> xu;
+  xu.init(x, [&](int R) {
+    int p = sorted_pair[tl.row0 + min(R, tl.rows - 1)];
+    p = min(max(p, 0), P - 1);
+    return static_cast<size_t>(p / k) * H;
+  });
+
+  f32x4_t acc[MB][2][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int gu = 0; gu < 2; ++gu)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) acc[mb][gu][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  xu.load(0);
+  xu.store(xs[0]);
+  __syncthreads();
+  for (int u = 0; u < units; ++u) {
+    Scales<4> sc[MB][2];
+    TRaw<WF> raw[MB][2];
+    if constexpr (WF != WF_BF16) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        sc[mb][0] = tscales(sg, nb0 + mb, H, u, r);
+        sc[mb][1] = tscales(su, nb0 + mb, H, u, r);
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      raw[mb][0] = tload<WF>(wg, nb0 + mb, H, u, lane);
+      raw[mb][1] = tload<WF>(wu, nb0 + mb, H, u, lane);
+    }
+    if (u + 1 < units) xu.load(u + 1);
+    SCHED_FENCE();
+    const char* buf = xs[u & 1];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      u32x4_t xa[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) xa[b] = xfrag<NB>(buf, st, b, lane);
+      f32x4_t corr[NB];
+      if constexpr (WF != WF_BF16) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          corr[b] = mfma_bf16(xa[b], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int gu = 0; gu < 2; ++gu) {
+          const u32x4_t wv = tdecode<WF>(raw[mb][gu], st);
+          if constexpr (WF == WF_BF16) {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[mb][gu][b] = mfma_bf16(xa[b], wv, acc[mb][gu][b]);
+          } else {
+            const float sv = fp16_to_f32(sc[mb][gu].s[st]);
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+              const f32x4_t pp = mfma_bf16(xa[b], wv, corr[b]);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[mb][gu][b][j] = fmaf(sv, pp[j], acc[mb][gu][b][j]);
+            }
+          }
+        }
+      }
+    }
+    if (u + 1 < units) xu.store(xs[(u + 1) & 1]);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int i = i0 + mb * 16 + r;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = b * 16 + 4 * q + j;
+        if (rr < tl.rows)
+          h[static_cast<size_t>(tl.row0 + rr) * I + i] =
+              f32_to_bf16(silu(acc[mb][0][b][j]) * acc[mb][1][b][j]);
+      }
+  }
+}
+
+// down with the intermediate rows staged through LDS (same scheme, K = I).
+template <int WF, int NB, int MB>
+__global__ __launch_bounds__(256) void k_down_x(const uint16_t* __restrict__ h,
+                                                const uint8_t* __restrict__ wd,
+                                                const uint16_t* __restrict__ sd,
+                                                const int32_t* __restrict__ tiles, int max_tiles,
+                                                int H, int I, uint16_t* __restrict__ y, int band,
+                                                int xcd) {
+  __shared__ __align__(16) char xs[2][NB * 4096];
+  int ti, sl;
+  if (!tile_item(tiles[3 * max_tiles], H / (64 * MB), band, xcd != 0, ti, sl)) return;
+  const Tile tl = read_tile(tiles, ti);
+  if (tl.rows <= 0) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, q = lane >> 4;
+  const int n0 = (sl * 4 + wave) * 16 * MB;
+  const int units = I / 128;
+  const size_t nb0 = (static_cast<size_t>(tl.e) * H + n0) / 16;
+
+  XUnit<NB> xu;
+  xu.init(h, [&](int R) { return static_cast<size_t>(tl.row0 + min(R, tl.rows - 1)) * I; });
+
+  f32x4_t acc[MB][NB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) acc[mb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  xu.load(0);
+  xu.store(xs[0]);
+  __syncthreads();
+  for (int u = 0; u < units; ++u) {
+    Scales<4> sc[MB];
+    TRaw<WF> raw[MB];
+    if constexpr (WF != WF_BF16) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) sc[mb] = tscales(sd, nb0 + mb, I, u, r);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) raw[mb] = tload<WF>(wd, nb0 + mb, I, u, lane);
+    if (u + 1 < units) xu.load(u + 1);
+    SCHED_FENCE();
+    const char* buf = xs[u & 1];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      u32x4_t ha[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) ha[b] = xfrag<NB>(buf, st, b, lane);
+      f32x4_t corr[NB];
+      if constexpr (WF != WF_BF16) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          corr[b] = mfma_bf16(ha[b], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const u32x4_t wv = tdecode<WF>(raw[mb], st);
+        if constexpr (WF == WF_BF16) {
+#pragma unroll
+          for (int b = 0; b < NB; ++b) acc[mb][b] = mfma_bf16(ha[b], wv, acc[mb][b]);
+        } else {
+          const float sv = fp16_to_f32(sc[mb].s[st]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) {
+            const f32x4_t pp = mfma_bf16(ha[b], wv, corr[b]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[mb][b][j] = fmaf(sv, pp[j], acc[mb][b][j]);
+          }
+        }
+      }
+    }
+    if (u + 1 < units) xu.store(xs[(u + 1) & 1]);
+    __syncthreads();
+  }
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int n = n0 + mb * 16 + r;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = b * 16 + 4 * q + j;
+        if (rr < tl.rows) y[static_cast<size_t>(tl.row0 + rr) * H + n] = f32_to_bf16(acc[mb][b][j]);
+      }
+  }
+}
+
 // float32 path (act and weights float32): one thread per output, float32
 // fused multiply-adds in ascending k.  grid (max_tiles, ceil(N/16)),
 // block 256 = 16 rows x 16 outputs.
@@ -819,11 +1023,21 @@ static void gateup_tiled_launch(const moe_shape& s, const Plan& pl, const void* 
                                 const int32_t* tiles, void* h, hipStream_t st) {
   const int nslices = s.I / (16 * MB * (4 / KSPLIT));
   const TileOrder o = tile_order(pl, true);
-  hipLaunchKernelGGL((k_gateup_t<WF, NB, KSPLIT, MB, kPrefetch<WF>>), item_grid(pl, nslices),
-                     dim3(256), 0, st, static_cast<const uint16_t*>(x),
-                     static_cast<const uint8_t*>(ex.gate), static_cast<const uint8_t*>(ex.up),
-                     ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair, s.top_k, s.H,
-                     s.I, s.T * s.top_k, static_cast<uint16_t*>(h), min(o.band, pl.max_tiles), o.xcd);
+  if constexpr (KSPLIT == 1 && NB >= 4) {
+    // large batches: token tile staged through LDS once per workgroup
+    hipLaunchKernelGGL((k_gateup_x<WF, NB, MB>), item_grid(pl, nslices), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(x), static_cast<const uint8_t*>(ex.gate),
+                       static_cast<const uint8_t*>(ex.up), ex.gate_scale, ex.up_scale, tiles,
+                       pl.max_tiles, sorted_pair, s.top_k, s.H, s.I, s.T * s.top_k,
+                       static_cast<uint16_t*>(h), min(o.band, pl.max_tiles), o.xcd);
+  } else {
+    hipLaunchKernelGGL((k_gateup_t<WF, NB, KSPLIT, MB, kPrefetch<WF>>), item_grid(pl, nslices),
+                       dim3(256), 0, st, static_cast<const uint16_t*>(x),
+                       static_cast<const uint8_t*>(ex.gate), static_cast<const uint8_t*>(ex.up),
+                       ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair, s.top_k, s.H,
+                       s.I, s.T * s.top_k, static_cast<uint16_t*>(h), min(o.band, pl.max_tiles),
+                       o.xcd);
+  }
 }
 
 template <int WF, int NB, int KSPLIT>
@@ -874,10 +1088,17 @@ static void down_tiled_launch(const moe_shape& s, const Plan& pl, const void* h,
                               const moe_experts& ex, const int32_t* tiles, void* y,
                               hipStream_t st) {
   const TileOrder o = tile_order(pl, false);
-  hipLaunchKernelGGL((k_down_t<WF, NB, MB, kPrefetch<WF>>), item_grid(pl, s.H / (64 * MB)),
-                     dim3(256), 0, st, static_cast<const uint16_t*>(h),
-                     static_cast<const uint8_t*>(ex.down), ex.down_scale, tiles, pl.max_tiles, s.H,
-                     s.I, static_cast<uint16_t*>(y), min(o.band, pl.max_tiles), o.xcd);
+  if constexpr (NB >= 4) {
+    hipLaunchKernelGGL((k_down_x<WF, NB, MB>), item_grid(pl, s.H / (64 * MB)), dim3(256), 0, st,
+                       static_cast<const uint16_t*>(h), static_cast<const uint8_t*>(ex.down),
+                       ex.down_scale, tiles, pl.max_tiles, s.H, s.I, static_cast<uint16_t*>(y),
+                       min(o.band, pl.max_tiles), o.xcd);
+  } else {
+    hipLaunchKernelGGL((k_down_t<WF, NB, MB, kPrefetch<WF>>), item_grid(pl, s.H / (64 * MB)),
+                       dim3(256), 0, st, static_cast<const uint16_t*>(h),
+                       static_cast<const uint8_t*>(ex.down), ex.down_scale, tiles, pl.max_tiles,
+                       s.H, s.I, static_cast<uint16_t*>(y), min(o.band, pl.max_tiles), o.xcd);
+  }
 }
 
 template <int WF, int NB>

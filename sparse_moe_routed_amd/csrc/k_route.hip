@@ -82,91 +82,101 @@ __global__ __launch_bounds__(1024) void k_router_parts(const uint16_t* __restric
   }
 }
 
-// Large batches: each wave owns a 32-token x 32-expert tile (2 x 2 MFMA
-// tiles) and walks all parts itself, keeping a float64 part sum and a float64
-// total per output (same association as above).  grid (ceil(T/64),
-// ceil(E/64)), block 256 (waves 2 x 2 over the 64 x 64 workgroup tile).
-__global__ __launch_bounds__(256) void k_router_tiles(const uint16_t* __restrict__ x,
-                                                      const uint16_t* __restrict__ wr,
-                                                      const float* __restrict__ bias, int T, int H,
-                                                      int E, int nparts,
-                                                      float* __restrict__ logits) {
+// Larger batches: workgroup tile of 32 A tokens x 32 A experts, four waves
+// in 2 x 2, each (16 A) x (16 A).  Token rows and router rows are staged in
+// LDS once per workgroup and 128-wide k unit (in MFMA fragment order), and
+// each wave walks the 32-wide chunks in k order, keeping a float64 part sum
+// and a float64 total per output (the association above).  Two LDS buffers:
+// the next unit is loaded while the current one is multiplied.
+// grid (ceil(T / 32 A), ceil(E / 32 A)), block 256.
+template <int A>
+__global__ __launch_bounds__(256) void k_router_lds(const uint16_t* __restrict__ x,
+                                                    const uint16_t* __restrict__ wr,
+                                                    const float* __restrict__ bias, int T, int H,
+                                                    int E, int nparts,
+                                                    float* __restrict__ logits) {
+  constexpr int NB = 2 * A;   // 16-row blocks per staged tile
+  __shared__ __align__(16) char xs[2][NB * 4096];
+  __shared__ __align__(16) char wsm[2][NB * 4096];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
-  const int t0 = blockIdx.x * 64 + (wave & 1) * 32;
-  const int e0 = blockIdx.y * 64 + (wave >> 1) * 32;
-  if (t0 >= T || e0 >= E) return;
+  const int tb = blockIdx.x * 32 * A, eb = blockIdx.y * 32 * A;
+  const int tblk = (wave & 1) * A, eblk = (wave >> 1) * A;
   const int cpp = H / 32 / nparts;
-  const uint16_t* xp[2];
-  const uint16_t* wp[2];
+  const int units = H / 128;
+
+  XUnit<NB> xu, wu;
+  xu.init(x, [&](int R) { return static_cast<size_t>(min(tb + R, T - 1)) * H; });
+  wu.init(wr, [&](int R) { return static_cast<size_t>(min(eb + R, E - 1)) * H; });
+
+  double part[A][A][4], tot[A][A][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    xp[i] = x + static_cast<size_t>(min(t0 + 16 * i + r, T - 1)) * H + q * 8;
-    wp[i] = wr + static_cast<size_t>(min(e0 + 16 * i + r, E - 1)) * H + q * 8;
-  }
-  double tot[2][2][4], part[2][2][4];
+  for (int a = 0; a < A; ++a)
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int i = 0; i < A; ++i)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) tot[a][b][j] = 0.0;
+      for (int j = 0; j < 4; ++j) part[a][i][j] = tot[a][i][j] = 0.0;
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  for (int pidx = 0; pidx < nparts; ++pidx) {
+
+  xu.load(0);
+  wu.load(0);
+  xu.store(xs[0]);
+  wu.store(wsm[0]);
+  __syncthreads();
+  for (int u = 0; u < units; ++u) {
+    if (u + 1 < units) {
+      xu.load(u + 1);
+      wu.load(u + 1);
+    }
+    const char* bx = xs[u & 1];
+    const char* bw = wsm[u & 1];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int st = 0; st < 4; ++st) {
+      u32x4_t xa[A], wa[A];
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+      for (int i = 0; i < A; ++i) xa[i] = xfrag<NB>(bx, st, tblk + i, lane);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) part[a][b][j] = 0.0;
-    const int kb = pidx * cpp * 32;
-    for (int c = 0; c < cpp; c += 4) {
-      u32x4_t wa[4][2], xb[4][2];
+      for (int a = 0; a < A; ++a) wa[a] = xfrag<NB>(bw, st, eblk + a, lane);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (c + u < cpp) {
+      for (int a = 0; a < A; ++a)
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            wa[u][i] = ld16(wp[i] + kb + (c + u) * 32);
-            xb[u][i] = ld16(xp[i] + kb + (c + u) * 32);
-          }
+        for (int i = 0; i < A; ++i) {
+          const f32x4_t f = mfma_bf16(wa[a], xa[i], zero);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) part[a][i][j] += static_cast<double>(f[j]);
         }
-      }
+      if ((4 * u + st + 1) % cpp == 0) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (c + u < cpp) {
+        for (int a = 0; a < A; ++a)
 #pragma unroll
-          for (int a = 0; a < 2; ++a)
+          for (int i = 0; i < A; ++i)
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              const f32x4_t f = mfma_bf16(wa[u][a], xb[u][b], zero);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) part[a][b][j] += static_cast<double>(f[j]);
+            for (int j = 0; j < 4; ++j) {
+              tot[a][i][j] += part[a][i][j];
+              part[a][i][j] = 0.0;
             }
-        }
       }
     }
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) tot[a][b][j] += part[a][b][j];
+    if (u + 1 < units) {
+      xu.store(xs[(u + 1) & 1]);
+      wu.store(wsm[(u + 1) & 1]);
+    }
+    __syncthreads();
   }
-  // lane holds experts e0 + 16a + 4q + j of token t0 + 16b + r
+  // lane holds experts eb + 16 (eblk + a) + 4 q + j of token tb + 16 (tblk + i) + r
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int t = t0 + 16 * b + r;
+  for (int i = 0; i < A; ++i) {
+    const int t = tb + 16 * (tblk + i) + r;
     if (t >= T) continue;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < A; ++a)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int e = e0 + 16 * a + 4 * q + j;
+        const int e = eb + 16 * (eblk + a) + 4 * q + j;
         if (e < E) {
-          double s = tot[a][b][j];
-          if (bias) s += static_cast<double>(bias[e]);
-          logits[static_cast<size_t>(t) * E + e] = static_cast<float>(s);
+          double sum = tot[a][i][j];
+          if (bias) sum += static_cast<double>(bias[e]);
+          logits[static_cast<size_t>(t) * E + e] = static_cast<float>(sum);
         }
       }
   }
@@ -265,9 +275,13 @@ hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const
       dim3 grid((s.T + 15) / 16, (s.E + 15) / 16);
       hipLaunchKernelGGL(k_router_parts, grid, dim3(64 * np), 0, st, static_cast<const uint16_t*>(x),
                          static_cast<const uint16_t*>(w_router), bias, s.T, s.H, s.E, np, lg);
+    } else if (s.T <= 1024) {
+      dim3 grid((s.T + 31) / 32, (s.E + 31) / 32);
+      hipLaunchKernelGGL(k_router_lds<1>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x),
+                         static_cast<const uint16_t*>(w_router), bias, s.T, s.H, s.E, np, lg);
     } else {
       dim3 grid((s.T + 63) / 64, (s.E + 63) / 64);
-      hipLaunchKernelGGL(k_router_tiles, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x),
+      hipLaunchKernelGGL(k_router_lds<2>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x),
                          static_cast<const uint16_t*>(w_router), bias, s.T, s.H, s.E, np, lg);
     }
   } else {

@@ -118,6 +118,49 @@ __device__ __forceinline__ u32x4_t dequant_int2_offset(uint32_t w16) {
   return r;
 }
 
+// Staging of activation rows through LDS (256-thread workgroups, 16-row
+// blocks, 128-wide k units of bf16).
+// Per-thread share of one unit: NB 16-byte chunks.  Chunk i of thread
+// (wave w, lane l) is row 16 i + 4 w + l / 16, k chunk l % 16 of the unit.
+// LDS layout: fragment f = st * NB + b holds 64 16-byte slots; the chunk of
+// MFMA lane r + 16 q sits in slot 16 q + (r ^ (4 st + q)).  The XOR keeps the
+// 16 lanes that store one row segment, and the 16 lanes that read one
+// fragment quarter, on 16 distinct bank groups.
+template <int NB>
+struct XUnit {
+  const uint16_t* src[NB];   // row base + chunk offset (elements)
+  int dst[NB];               // byte offset in one LDS buffer
+  u32x4_t v[NB];
+
+  // `row_of(R)` gives the element offset of tile row R (clamped by caller)
+  template <typename RowOf>
+  __device__ __forceinline__ void init(const uint16_t* base, RowOf row_of) {
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int c = l & 15, r = 4 * w + (l >> 4);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      src[i] = base + row_of(16 * i + r) + c * 8;
+      dst[i] = (((c >> 2) * NB + i) * 64 + 16 * (c & 3) + (r ^ c)) * 16;
+    }
+  }
+  __device__ __forceinline__ void load(int u) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) v[i] = ld16(src[i] + 128 * u);
+  }
+  __device__ __forceinline__ void store(char* buf) const {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) *reinterpret_cast<u32x4_t*>(buf + dst[i]) = v[i];
+  }
+};
+
+// A fragment (k chunk st, row block b) of the staged unit in `buf`.
+template <int NB>
+__device__ __forceinline__ u32x4_t xfrag(const char* buf, int st, int b, int lane) {
+  const int q = lane >> 4, r = lane & 15;
+  return *reinterpret_cast<const u32x4_t*>(
+      buf + ((st * NB + b) * 64 + 16 * q + (r ^ (4 * st + q))) * 16);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, kWave);

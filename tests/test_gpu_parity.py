@@ -31,6 +31,9 @@ SMALL = {
     "int2_small": C5.with_(T=16, H=512, E=64, I=128, layers=1),
     "int4_many_rows": C4.with_(T=1500, H=256, E=16, I=128, k=4, layers=1),
     "int2_ksplit_rows": C5.with_(T=600, H=384, E=24, I=96, k=3, layers=1, bias="none"),
+    # LDS-staged router with a ragged expert tile and parts that end inside
+    # a 128-wide k unit (H/32 = 20 chunks, 10 parts of 2)
+    "router_ragged_parts": C3.with_(T=200, H=640, E=100, I=128, k=6),
 }
 
 _cache = {}

@@ -18,10 +18,13 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 ARCH = "gfx950"
 
-# packed-fp32 instructions are disabled for all device code
+# packed-fp32 instructions are disabled for all device code; MFMA results go
+# to VGPRs (the low-bit kernels scale each MFMA result with VALU FMAs, and the
+# default AGPR destinations cost one v_accvgpr_read per element)
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result", "-Wno-pass-failed",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 

@@ -121,12 +121,16 @@ typedef struct {
  * with nb < N/16, r < 16, q < 4, j < 8:
  *   bf16: element W[16nb + r][32ks + 8q + j] at element index
  *         ((nb*(K/32) + ks)*64 + 16q + r)*8 + j           (ks < K/32);
- *   int4/int2: the 8 codes c_j = W[16nb + r][128kb + 32s + 8q + j] (j = 0..7)
- *         at byte offset ((nb*(K/128) + kb)*64 + 16q + r)*B + s*(B/4)
- *         (kb < K/128, s < 4, B = 16 for int4, 8 for int2), packed as:
- *         int2: 2 bytes, c_j at bits 2j..2j+1 (the row-major packing);
- *         int4: 4 bytes, c_2m at nibble m and c_2m+1 at nibble m+4 (m < 4),
- *         so that one mask extracts a (c_2m, c_2m+1) pair;
+ *   int4/int2: the 8 codes c_j = W[16nb + r][128kb + 32s + 8q + j] (j = 0..7,
+ *         kb < K/128, s < 4) of lane unit u = (nb*(K/128) + kb)*64 + 16q + r
+ *         are stored offset-binary (c + 8 for int4, c + 2 for int2) in the
+ *         B bytes at byte offset u*B (B = 16 for int4, 8 for int2), read as
+ *         little-endian 32-bit words:
+ *         int4: word s holds c_2m at nibble m and c_2m+1 at nibble m+4 (m < 4);
+ *         int2: word s/2 holds c_2m at bits 8(s%2) + 2m and c_2m+1 at bits
+ *         16 + 8(s%2) + 2m (m < 4);
+ *         so that one mask and one OR turn a (c_2m, c_2m+1) pair into two
+ *         bf16 values;
  *   scales: scale[16nb + r][4kb + s] at fp16 index ((nb*(K/128) + kb)*16 + r)*4 + s.
  * Requirements: bf16 activations; I % 128 == 0 (MOE_E_SHAPE otherwise). */
 

@@ -390,14 +390,20 @@ __device__ __forceinline__ TRaw<WF> tload(const uint8_t* mat, size_t nb, int K, 
 }
 
 template <int WF>
-__device__ __forceinline__ u32x4_t tdecode(const TRaw<WF>& t, int s) {
+__device__ __forceinline__ Dq dq_consts() {
+  if constexpr (WF == WF_BF16) return Dq{0u, 0u};   // unused
+  else return Dq{in_vgpr(WF == WF_INT4 ? 0x000F000Fu : 0x00030003u), in_vgpr(0x43004300u)};
+}
+
+template <int WF>
+__device__ __forceinline__ u32x4_t tdecode(const TRaw<WF>& t, int s, Dq d) {
   if constexpr (WF == WF_BF16) {
     return t.v[s];
   } else if constexpr (WF == WF_INT4) {
-    return dequant_int4_offset(t.v[0][s]);
+    return dequant_int4_tiled(t.v[0][s], d);
   } else {
-    const uint32_t d = t.v[0][s >> 1];
-    return dequant_int2_offset((s & 1) ? (d >> 16) : d);
+    const uint32_t w = t.v[0][s >> 1];
+    return (s & 1) ? dequant_int2_tiled<1>(w, d) : dequant_int2_tiled<0>(w, d);
   }
 }
 
@@ -434,6 +440,7 @@ __global__ __launch_bounds__(256) void k_gateup_t(
   if (tl.rows <= 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
+  const Dq dq = dq_consts<WF>();
   const int kp = wave % KSPLIT, rg = wave / KSPLIT;
   const int i0 = (sl * RG + rg) * 16 * MB;
   const int units = H / 128 / KSPLIT;
@@ -493,7 +500,7 @@ __global__ __launch_bounds__(256) void k_gateup_t(
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int gu = 0; gu < 2; ++gu) {
-          const u32x4_t wv = tdecode<WF>(S.raw[mb][gu], st);
+          const u32x4_t wv = tdecode<WF>(S.raw[mb][gu], st, dq);
           if constexpr (WF == WF_BF16) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[mb][gu][b] = mfma_bf16(S.xa[st][b], wv, acc[mb][gu][b]);
@@ -595,6 +602,7 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
   if (tl.rows <= 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
+  const Dq dq = dq_consts<WF>();
   const int n0 = (sl * 4 + wave) * 16 * MB;
   const size_t nb0 = (static_cast<size_t>(tl.e) * H + n0) / 16;
   const uint16_t* ph[NB];
@@ -636,7 +644,7 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const u32x4_t wv = tdecode<WF>(S.raw[mb], st);
+        const u32x4_t wv = tdecode<WF>(S.raw[mb], st, dq);
         if constexpr (WF == WF_BF16) {
 #pragma unroll
           for (int b = 0; b < NB; ++b) acc[mb][b] = mfma_bf16(S.ha[st][b], wv, acc[mb][b]);
@@ -714,6 +722,7 @@ __global__ __launch_bounds__(256) void k_gateup_x(
   if (tl.rows <= 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
+  const Dq dq = dq_consts<WF>();
   const int i0 = (sl * 4 + wave) * 16 * MB;
   const int units = H / 128;
   const size_t nb0 = (static_cast<size_t>(tl.e) * I + i0) / 16;
@@ -769,7 +778,7 @@ __global__ __launch_bounds__(256) void k_gateup_x(
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int gu = 0; gu < 2; ++gu) {
-          const u32x4_t wv = tdecode<WF>(raw[mb][gu], st);
+          const u32x4_t wv = tdecode<WF>(raw[mb][gu], st, dq);
           if constexpr (WF == WF_BF16) {
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[mb][gu][b] = mfma_bf16(xa[b], wv, acc[mb][gu][b]);
@@ -819,6 +828,7 @@ __global__ __launch_bounds__(256) void k_down_x(const uint16_t* __restrict__ h,
   if (tl.rows <= 0) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
+  const Dq dq = dq_consts<WF>();
   const int n0 = (sl * 4 + wave) * 16 * MB;
   const int units = I / 128;
   const size_t nb0 = (static_cast<size_t>(tl.e) * H + n0) / 16;
@@ -860,7 +870,7 @@ __global__ __launch_bounds__(256) void k_down_x(const uint16_t* __restrict__ h,
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const u32x4_t wv = tdecode<WF>(raw[mb], st);
+        const u32x4_t wv = tdecode<WF>(raw[mb], st, dq);
         if constexpr (WF == WF_BF16) {
 #pragma unroll
           for (int b = 0; b < NB; ++b) acc[mb][b] = mfma_bf16(ha[b], wv, acc[mb][b]);

@@ -35,21 +35,42 @@ __global__ __launch_bounds__(256) void k_tile_codes(const uint8_t* __restrict__ 
   const int r = l & 15, q = l >> 4;
   const size_t row = (nb * 16 + r) * (static_cast<size_t>(K) * BITS / 8);
   uint8_t* o = dst + idx * (4 * BITS);
+  uint32_t piece[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const size_t b = row + (kb * 128 + s * 32 + q * 8) * BITS / 8;
-    if constexpr (BITS == 4) {
-      // natural nibble order c0..c7 -> tiled order (nibble m: c_2m, nibble m+4: c_2m+1)
-      const uint32_t v = *reinterpret_cast<const uint32_t*>(src + b);
+    piece[s] = BITS == 4 ? *reinterpret_cast<const uint32_t*>(src + b)
+                         : *reinterpret_cast<const uint16_t*>(src + b);
+  }
+  if constexpr (BITS == 4) {
+    // natural nibble order c0..c7 -> stored c_2m at nibble m, c_2m+1 at
+    // nibble m+4; two's complement -> offset binary (xor 8)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
       uint32_t t = 0;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        t |= ((v >> (8 * m)) & 0xFu) << (4 * m);
-        t |= ((v >> (8 * m + 4)) & 0xFu) << (4 * (m + 4));
+        t |= ((piece[s] >> (8 * m)) & 0xFu) << (4 * m);
+        t |= ((piece[s] >> (8 * m + 4)) & 0xFu) << (4 * (m + 4));
       }
-      *reinterpret_cast<uint32_t*>(o + s * 4) = t;
-    } else {
-      *reinterpret_cast<uint16_t*>(o + s * 2) = *reinterpret_cast<const uint16_t*>(src + b);
+      *reinterpret_cast<uint32_t*>(o + s * 4) = t ^ 0x88888888u;
+    }
+  } else {
+    // chunks 2w and 2w+1 share word w: chunk sub's c_2m at bits 8 sub + 2m,
+    // c_2m+1 at bits 16 + 8 sub + 2m; two's complement -> offset binary (xor 2)
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      uint32_t t = 0;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        const uint32_t v = piece[2 * w + sub];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          t |= ((v >> (4 * m)) & 3u) << (8 * sub + 2 * m);
+          t |= ((v >> (4 * m + 2)) & 3u) << (16 + 8 * sub + 2 * m);
+        }
+      }
+      *reinterpret_cast<uint32_t*>(o + w * 4) = t ^ 0xAAAAAAAAu;
     }
   }
 }

@@ -93,28 +93,42 @@ __device__ __forceinline__ u32x4_t dequant_int2x8(uint32_t w16) {
 constexpr uint32_t kNegOffset4 = 0xC308C308u;   // bf16 pair (-136, -136)
 constexpr uint32_t kNegOffset2 = 0xC302C302u;   // bf16 pair (-130, -130)
 
-// 8 int4 codes in the tiled nibble order (nibble m: code 2m, nibble m+4:
-// code 2m+1) -> 4 bf16 pairs (136 + q_2m, 136 + q_2m+1), m = 0..3.
-__device__ __forceinline__ u32x4_t dequant_int4_offset(uint32_t w) {
-  const uint32_t t = w ^ 0x88888888u;
+// Tiled low-bit codes are stored offset-binary (code + 8 for int4, code + 2
+// for int2), so one AND with a field mask and one OR with 0x4300 per bf16
+// half give the exact bf16 value 128 + stored code.  The mask and the magic
+// word arrive in registers: gfx9 VOP3 instructions take no literal operand,
+// so with constants the AND-OR would split into two instructions.
+struct Dq {
+  uint32_t mask, magic;
+};
+
+// Moves a constant into a VGPR the compiler cannot fold back into literals.
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// int4: one 32-bit word per k chunk, stored code 2m at nibble m and code
+// 2m+1 at nibble m+4 -> 4 bf16 pairs (136 + q_2m, 136 + q_2m+1).
+__device__ __forceinline__ u32x4_t dequant_int4_tiled(uint32_t w, Dq d) {
   u32x4_t r;
-  r[0] = (t & 0x000F000Fu) | 0x43004300u;
-  r[1] = ((t >> 4) & 0x000F000Fu) | 0x43004300u;
-  r[2] = ((t >> 8) & 0x000F000Fu) | 0x43004300u;
-  r[3] = ((t >> 12) & 0x000F000Fu) | 0x43004300u;
+  r[0] = (w & d.mask) | d.magic;
+  r[1] = ((w >> 4) & d.mask) | d.magic;
+  r[2] = ((w >> 8) & d.mask) | d.magic;
+  r[3] = ((w >> 12) & d.mask) | d.magic;
   return r;
 }
 
-// 8 int2 codes (natural order, 2 bits each, low bits first) -> 4 bf16 pairs
-// (130 + q_2m, 130 + q_2m+1).
-__device__ __forceinline__ u32x4_t dequant_int2_offset(uint32_t w16) {
-  const uint32_t t = (w16 & 0xFFFFu) ^ 0xAAAAu;
-  const uint32_t u = t | (t << 14);
+// int2: one 32-bit word per pair of k chunks; chunk `sub` (0, 1) has stored
+// code 2m at bits 8 sub + 2m and code 2m+1 at bits 16 + 8 sub + 2m ->
+// 4 bf16 pairs (130 + q_2m, 130 + q_2m+1).
+template <int SUB>
+__device__ __forceinline__ u32x4_t dequant_int2_tiled(uint32_t w, Dq d) {
   u32x4_t r;
-  r[0] = (u & 0x00030003u) | 0x43004300u;
-  r[1] = ((u >> 4) & 0x00030003u) | 0x43004300u;
-  r[2] = ((u >> 8) & 0x00030003u) | 0x43004300u;
-  r[3] = ((u >> 12) & 0x00030003u) | 0x43004300u;
+  r[0] = ((w >> (8 * SUB)) & d.mask) | d.magic;
+  r[1] = ((w >> (8 * SUB + 2)) & d.mask) | d.magic;
+  r[2] = ((w >> (8 * SUB + 4)) & d.mask) | d.magic;
+  r[3] = ((w >> (8 * SUB + 6)) & d.mask) | d.magic;
   return r;
 }
 

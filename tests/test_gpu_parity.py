@@ -446,15 +446,27 @@ def test_tile_layout_bit_exact(wfmt):
     sync()
     src, dst = case.li.experts, case.tiled_keep
 
-    def int4_split_nibbles(v):
-        """natural nibble order c0..c7 of each 4-byte piece -> c_2m at nibble m,
-        c_2m+1 at nibble m+4"""
+    def int4_words(v):
+        """each 4-byte piece (natural nibble order c0..c7, two's complement)
+        -> one word: c_2m at nibble m, c_2m+1 at nibble m+4, offset binary"""
         d = np.ascontiguousarray(v).reshape(-1, 4).copy().view(np.uint32).reshape(-1).astype(np.uint64)
         out = np.zeros_like(d)
         for m in range(4):
             out |= ((d >> (8 * m)) & 0xF) << (4 * m)
             out |= ((d >> (8 * m + 4)) & 0xF) << (4 * (m + 4))
-        return out.astype(np.uint32).view(np.uint8)
+        return (out.astype(np.uint32) ^ np.uint32(0x88888888)).view(np.uint8)
+
+    def int2_words(v):
+        """pieces of 2 bytes (c_j at bits 2j, two's complement), 4 per lane
+        unit -> 2 words: piece 2w+sub's c_2m at bits 8 sub + 2m and c_2m+1 at
+        bits 16 + 8 sub + 2m of word w, offset binary"""
+        p = np.ascontiguousarray(v).reshape(-1, 2, 2, 2).copy().view(np.uint16)[..., 0].astype(np.uint64)
+        out = np.zeros(p.shape[:2], dtype=np.uint64)               # [units, w]
+        for sub in range(2):
+            for m in range(4):
+                out |= ((p[:, :, sub] >> (4 * m)) & 3) << (8 * sub + 2 * m)
+                out |= ((p[:, :, sub] >> (4 * m + 2)) & 3) << (16 + 8 * sub + 2 * m)
+        return (out.astype(np.uint32) ^ np.uint32(0xAAAAAAAA)).reshape(-1).view(np.uint8)
 
     def arrange(a, N, K):
         if wfmt == "dense":                                   # [E*N][K] elements
@@ -462,7 +474,7 @@ def test_tile_layout_bit_exact(wfmt):
             return np.ascontiguousarray(v).reshape(-1)
         B = 4 if wfmt == "int4_g32" else 2                    # bytes per 8 codes
         v = np.ascontiguousarray(a.reshape(-1, 16, K // 128, 4, 4, B).transpose(0, 2, 4, 1, 3, 5))
-        return int4_split_nibbles(v) if wfmt == "int4_g32" else v.reshape(-1)
+        return int4_words(v) if wfmt == "int4_g32" else int2_words(v)
 
     def arrange_scales(a, K):
         v = a.reshape(-1, 16, K // 128, 4).transpose(0, 2, 1, 3)

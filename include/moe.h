@@ -24,9 +24,12 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  * - All tensor pointers are DEVICE pointers (hipMalloc / torch CUDA memory)
- *   owned by the caller; the library never allocates device memory and keeps
- *   no state between calls.  Scratch memory is the caller's workspace of at
- *   least moe_workspace_size(shape) bytes (NULL allowed when that is 0).
+ *   owned by the caller; the library never allocates device memory.  Scratch
+ *   memory is the caller's workspace of at least moe_workspace_size(shape)
+ *   bytes (NULL allowed when that is 0); its contents need no initialisation.
+ *   Between calls a workspace carries only the FFN tile plan (from
+ *   moe_permute to moe_ffn_gate_up / moe_ffn_down); the library keeps no
+ *   other state.
  * - Every call only ENQUEUES work on `stream` (NULL = the null stream) and
  *   returns without synchronizing.  Calls on different streams with disjoint
  *   outputs and workspaces are independent.
@@ -196,9 +199,9 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids,
  *   y[r][n] = sum_i W_down[e][n][i] * silu(g_i) * u_i,
  *   g_i = sum_h W_gate[e][i][h] x[t][h],  u_i = sum_h W_up[e][i][h] x[t][h].
  * Each active expert's weights are streamed from memory once per call for
- * its whole row set when it has at most 64 rows (otherwise once per 64-row
- * tile).  perm: counts, offsets, sorted_pair, active, n_active are read
- * (pair_row is not used).  y [P][H] act (output, rows in permuted order).
+ * its whole row set when it has at most 16*nb rows, the tile height (nb as
+ * in the domain above), otherwise once per tile.  perm: counts, offsets,
+ * sorted_pair, active, n_active are read (pair_row is not used).  y [P][H] act (output, rows in permuted order).
  * The SwiGLU intermediate is kept in the act type (bf16 or float32). */
 int moe_grouped_ffn(const moe_shape* shape, const void* x,
                     const moe_experts* experts, const moe_perm* perm, void* y,

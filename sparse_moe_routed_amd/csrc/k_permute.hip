@@ -102,20 +102,15 @@ __device__ void emit_tiles(int nact, const int* s_act, const int* s_cnt, const i
   if (threadIdx.x == 0) tiles[3 * max_tiles] = min(total, max_tiles);
 }
 
-// Small batches: everything in one workgroup, one pass (E*W words of bitmap
-// plus E*W words of prefixes fit in LDS).
-__global__ __launch_bounds__(1024) void k_permute_small(
-    const int32_t* __restrict__ ids, int T, int k, int E, int W, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
-    int32_t* __restrict__ pair_row, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
-    int rt, int max_tiles, int32_t* __restrict__ tiles) {
-  extern __shared__ uint32_t dyn[];
-  __shared__ int s_cnt[1024];
-  __shared__ int s_off[1024];
-  __shared__ int s_act[1024];
-  __shared__ int s_tot[17];
-  uint32_t* bits = dyn;
-  uint32_t* pre = dyn + E * W;
+// Small batches: everything in one 1024-thread workgroup, one pass.  `ids`
+// may point to global memory or LDS; bits/pre hold E*W words each.
+__device__ void permute_small_body(const int32_t* ids, int T, int k, int E, int W,
+                                   int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                   int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_row,
+                                   int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+                                   int rt, int max_tiles, int32_t* __restrict__ tiles,
+                                   uint32_t* bits, uint32_t* pre, int* s_cnt, int* s_off,
+                                   int* s_act, int* s_tot) {
   const int tid = threadIdx.x;
   const int P = T * k;
 
@@ -153,6 +148,20 @@ __global__ __launch_bounds__(1024) void k_permute_small(
     sorted_pair[row] = p;
     pair_row[p] = row;
   }
+}
+
+__global__ __launch_bounds__(1024) void k_permute_small(
+    const int32_t* __restrict__ ids, int T, int k, int E, int W, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
+    int32_t* __restrict__ pair_row, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+    int rt, int max_tiles, int32_t* __restrict__ tiles) {
+  extern __shared__ uint32_t dyn[];
+  __shared__ int s_cnt[1024];
+  __shared__ int s_off[1024];
+  __shared__ int s_act[1024];
+  __shared__ int s_tot[17];
+  permute_small_body(ids, T, k, E, W, counts, offsets, sorted_pair, pair_row, active, n_active, rt,
+                     max_tiles, tiles, dyn, dyn + E * W, s_cnt, s_off, s_act, s_tot);
 }
 
 // Large batches: chunks of kChunkTok tokens.

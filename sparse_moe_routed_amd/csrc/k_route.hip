@@ -11,6 +11,7 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "route_device.h"
 
 namespace moe {
 
@@ -22,7 +23,6 @@ namespace moe {
 // bias is added, and the total is rounded once to float32.  Both kernels
 // below use exactly this association, so a token's logits are bit-identical
 // whatever the batch size or the kernel that computed them.
-constexpr int kRouterBatch = 8;
 
 // Small batches: one 16-token x 16-expert tile per workgroup, one wave per
 // part, part sums combined through LDS.  grid (ceil(T/16), ceil(E/16)),
@@ -33,53 +33,11 @@ __global__ __launch_bounds__(1024) void k_router_parts(const uint16_t* __restric
                                                        int H, int E, int nparts,
                                                        float* __restrict__ logits) {
   __shared__ double red[16][64][4];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int r = lane & 15, q = lane >> 4;
+  const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
-  const int cpp = H / 32 / nparts;
-  const int kbeg = wave * cpp * 32;
-  const int tt = min(t0 + r, T - 1);
-  const int ee = min(e0 + r, E - 1);
-  const uint16_t* xp = x + static_cast<size_t>(tt) * H + kbeg + q * 8;
-  const uint16_t* wp = wr + static_cast<size_t>(ee) * H + kbeg + q * 8;
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < cpp; c += kRouterBatch) {
-    u32x4_t a[kRouterBatch], b[kRouterBatch];
-#pragma unroll
-    for (int u = 0; u < kRouterBatch; ++u) {
-      if (c + u < cpp) {
-        a[u] = ld16(wp + (c + u) * 32);
-        b[u] = ld16(xp + (c + u) * 32);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kRouterBatch; ++u) {
-      if (c + u < cpp) {
-        const f32x4_t f = mfma_bf16(a[u], b[u], zero);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] += static_cast<double>(f[j]);
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) red[wave][lane][j] = acc[j];
+  router_part(x, wr, T, H, E, nparts, t0, e0, wave, red);
   __syncthreads();
-  if (wave == 0) {
-    const int t = t0 + r;
-    if (t < T) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = e0 + 4 * q + j;
-        if (e < E) {
-          double s = red[0][lane][j];
-          for (int w = 1; w < nparts; ++w) s += red[w][lane][j];
-          if (bias) s += static_cast<double>(bias[e]);
-          logits[static_cast<size_t>(t) * E + e] = static_cast<float>(s);
-        }
-      }
-    }
-  }
+  if (wave == 0) router_store(red, bias, T, E, nparts, t0, e0, logits);
 }
 
 // Larger batches: workgroup tile of 32 A tokens x 32 A experts, four waves
@@ -207,57 +165,16 @@ __global__ __launch_bounds__(256) void k_router_f32(const float* __restrict__ x,
   logits[idx] = static_cast<float>(s);
 }
 
-// Exact top-k per token, one wave per token; lane l holds the logits of
-// experts l, 64 + l, ... (NV slots, E <= 64 NV).  Each of the k rounds takes
-// the wave maximum m of the remaining logits, then the smallest expert index
-// whose logit equals m -- the total order (logit descending, index
-// ascending) -- with DPP row reductions and readlanes (no LDS round trips).
-// -0.0 and +0.0 compare equal.  Weights: exp(l_j - l_0) / sum over the
-// selected, in float32 (the full softmax renormalized over the selection).
+// Exact top-k, one wave per token (topk_token).  grid ceil(T/4), block 256.
 template <int NV>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
                                               int32_t* __restrict__ ids, float* __restrict__ w) {
   __shared__ float sel[4][1024];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;   // whole wave leaves; no workgroup barrier below
-  const float* lt = logits + static_cast<size_t>(t) * E;
-  float v[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) v[j] = lt[min(j * 64 + lane, E - 1)];
-  uint32_t live = 0;
-#pragma unroll
-  for (int j = 0; j < NV; ++j)
-    if (j * 64 + lane < E) live |= 1u << j;
-  for (int rnk = 0; rnk < k; ++rnk) {
-    float lm = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < NV; ++j)
-      if ((live >> j) & 1u) lm = fmaxf(lm, v[j]);
-    const float m = wave_max_f32(lm);
-    uint32_t li = 0xffffffffu;
-#pragma unroll
-    for (int j = NV - 1; j >= 0; --j)
-      if (((live >> j) & 1u) && v[j] == m) li = static_cast<uint32_t>(j * 64 + lane);
-    const uint32_t e = wave_min_u32(li);
-    if (static_cast<int>(e & 63u) == lane) live &= ~(1u << (e >> 6));
-    if (lane == 0) {
-      ids[static_cast<size_t>(t) * k + rnk] = static_cast<int32_t>(e);
-      sel[wave][rnk] = m;
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  const float m0 = sel[wave][0];
-  float part = 0.f;
-  for (int rnk = lane; rnk < k; rnk += 64) {
-    const float ex = expf(sel[wave][rnk] - m0);
-    sel[wave][rnk] = ex;
-    part += ex;
-  }
-  const float sum = wave_sum_f32(part);
-  for (int rnk = lane; rnk < k; rnk += 64) w[static_cast<size_t>(t) * k + rnk] = sel[wave][rnk] / sum;
+  const size_t o = static_cast<size_t>(t) * k;
+  topk_token<NV>(logits + static_cast<size_t>(t) * E, E, k, sel[wave], ids + o, w + o, nullptr);
 }
 
 template <int NV>
@@ -265,10 +182,8 @@ static void launch_topk(const moe_shape& s, const float* lg, int32_t* ids, float
   hipLaunchKernelGGL((k_topk<NV>), dim3((s.T + 3) / 4), dim3(256), 0, st, lg, s.T, s.E, s.top_k, ids, w);
 }
 
-hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const void* w_router,
-                        const float* bias, int32_t* ids, float* w, float* logits, void* ws,
-                        hipStream_t st) {
-  float* lg = logits ? logits : reinterpret_cast<float*>(static_cast<char*>(ws) + pl.logits_off);
+static hipError_t launch_router(const moe_shape& s, const void* x, const void* w_router,
+                                const float* bias, float* lg, hipStream_t st) {
   if (s.act == MOE_DT_BF16) {
     const int np = router_parts(s.H);
     if (s.T <= 64) {
@@ -290,6 +205,15 @@ hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const
                        static_cast<const float*>(x), static_cast<const float*>(w_router), bias, s.T,
                        s.H, s.E, lg);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const void* w_router,
+                        const float* bias, int32_t* ids, float* w, float* logits, void* ws,
+                        hipStream_t st) {
+  float* lg = logits ? logits : reinterpret_cast<float*>(static_cast<char*>(ws) + pl.logits_off);
+  hipError_t e = launch_router(s, x, w_router, bias, lg, st);
+  if (e != hipSuccess) return e;
   const int nv = (s.E + 63) / 64;
   if (nv <= 1) launch_topk<1>(s, lg, ids, w, st);
   else if (nv <= 2) launch_topk<2>(s, lg, ids, w, st);

@@ -424,8 +424,9 @@ __device__ __forceinline__ u32x4_t neg_offset_fragment() {
 // as 128 + offset + q; the C operand carries -offset * sum(x) (one MFMA of x
 // against a constant fragment per 32-k chunk, shared by all the wave's rows),
 // so each group partial is sum(q x) before its fp16 scale is applied.
-// grid (I / (16 * MB * 4 / KSPLIT), max_tiles), block 256.
-template <int WF, int NB, int KSPLIT, int MB, bool PF>
+// 1-D grid over (tile, slice) items, I / (16 MB 4 / KSPLIT) slices per tile;
+// block 256.
+template <int WF, int NB, int KSPLIT, int MB>
 __global__ __launch_bounds__(256) void k_gateup_t(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
     const uint16_t* __restrict__ sg, const uint16_t* __restrict__ su,
@@ -517,29 +518,11 @@ __global__ __launch_bounds__(256) void k_gateup_t(
       }
     }
   };
-  const int ue = ub + units;
-  if constexpr (PF) {
-    // two register stages: the next unit's loads are in flight while the
-    // current unit is computed
-    Stage s0, s1;
-    load(s0, ub);
-    for (int u = ub; u < ue; u += 2) {
-      if (u + 1 < ue) load(s1, u + 1);
-      SCHED_FENCE();
-      compute(s0);
-      if (u + 1 < ue) {
-        if (u + 2 < ue) load(s0, u + 2);
-        SCHED_FENCE();
-        compute(s1);
-      }
-    }
-  } else {
-    for (int u = ub; u < ue; ++u) {
-      Stage s0;
-      load(s0, u);
-      SCHED_FENCE();
-      compute(s0);
-    }
+  for (int u = ub; u < ub + units; ++u) {
+    Stage s0;
+    load(s0, u);
+    SCHED_FENCE();
+    compute(s0);
   }
 
   if constexpr (KSPLIT > 1) {
@@ -589,7 +572,7 @@ __global__ __launch_bounds__(256) void k_gateup_t(
 
 // down on tiled weights: MB 16-row blocks of output features per wave,
 // 64 MB per workgroup, full K = I.  1-D grid over (tile, slice) items, block 256.
-template <int WF, int NB, int MB, bool PF>
+template <int WF, int NB, int MB>
 __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
                                                 const uint8_t* __restrict__ wd,
                                                 const uint16_t* __restrict__ sd,
@@ -660,27 +643,11 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
       }
     }
   };
-  const int units = I / 128;
-  if constexpr (PF) {
-    Stage s0, s1;
-    load(s0, 0);
-    for (int u = 0; u < units; u += 2) {
-      if (u + 1 < units) load(s1, u + 1);
-      SCHED_FENCE();
-      compute(s0);
-      if (u + 1 < units) {
-        if (u + 2 < units) load(s0, u + 2);
-        SCHED_FENCE();
-        compute(s1);
-      }
-    }
-  } else {
-    for (int u = 0; u < units; ++u) {
-      Stage s0;
-      load(s0, u);
-      SCHED_FENCE();
-      compute(s0);
-    }
+  for (int u = 0; u < I / 128; ++u) {
+    Stage s0;
+    load(s0, u);
+    SCHED_FENCE();
+    compute(s0);
   }
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) {
@@ -982,21 +949,15 @@ static void launch_down_wf(const moe_shape& s, const Plan& pl, const void* h,
                        s.I, static_cast<uint16_t*>(y));
 }
 
-// Two-stage register prefetch across k units.  Measured on MI355X it loses
-// for every format at the row counts below (the second stage costs the
-// registers that more rows per wave -- fewer token loads per weight byte --
-// put to better use), so it is off; the path stays for other shapes.
-template <int WF>
-constexpr bool kPrefetch = false;
-
 // Rows per wave (16 MB) for the tiled kernels: bf16 keeps 32 rows (the raw
-// fragments are 64 B per lane per row block); low-bit formats take more rows
-// so that every token fragment feeds more MFMAs and each wave streams more
-// bytes.  These keep every launched variant within the 512-register wave
-// budget without spills.
+// fragments are 64 B per lane per row block); low-bit formats take 64 rows
+// (32 at 64-row token tiles) so that every token fragment feeds more MFMAs.
+// Measured on MI355X: 128 rows (int2 at 16-row tiles) leaves too few waves
+// to hide the dequant work (24 -> 28 us per 48-layer verify gate/up launch);
+// every launched variant stays within the register budget without spills.
 template <int WF, int NB>
 constexpr int tiled_mb_max() {
-  return WF == WF_BF16 ? 2 : (WF == WF_INT4 ? (NB >= 4 ? 2 : 4) : (8 / NB));
+  return WF == WF_BF16 ? 2 : (NB >= 4 ? 2 : 4);
 }
 
 // largest MB <= the maximum whose workgroup rows (rows_per_mb1 * MB) divide N
@@ -1041,7 +1002,7 @@ static void gateup_tiled_launch(const moe_shape& s, const Plan& pl, const void* 
                        pl.max_tiles, sorted_pair, s.top_k, s.H, s.I, s.T * s.top_k,
                        static_cast<uint16_t*>(h), min(o.band, pl.max_tiles), o.xcd);
   } else {
-    hipLaunchKernelGGL((k_gateup_t<WF, NB, KSPLIT, MB, kPrefetch<WF>>), item_grid(pl, nslices),
+    hipLaunchKernelGGL((k_gateup_t<WF, NB, KSPLIT, MB>), item_grid(pl, nslices),
                        dim3(256), 0, st, static_cast<const uint16_t*>(x),
                        static_cast<const uint8_t*>(ex.gate), static_cast<const uint8_t*>(ex.up),
                        ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair, s.top_k, s.H,
@@ -1104,7 +1065,7 @@ static void down_tiled_launch(const moe_shape& s, const Plan& pl, const void* h,
                        ex.down_scale, tiles, pl.max_tiles, s.H, s.I, static_cast<uint16_t*>(y),
                        min(o.band, pl.max_tiles), o.xcd);
   } else {
-    hipLaunchKernelGGL((k_down_t<WF, NB, MB, kPrefetch<WF>>), item_grid(pl, s.H / (64 * MB)),
+    hipLaunchKernelGGL((k_down_t<WF, NB, MB>), item_grid(pl, s.H / (64 * MB)),
                        dim3(256), 0, st, static_cast<const uint16_t*>(h),
                        static_cast<const uint8_t*>(ex.down), ex.down_scale, tiles, pl.max_tiles,
                        s.H, s.I, static_cast<uint16_t*>(y), min(o.band, pl.max_tiles), o.xcd);

@@ -371,19 +371,47 @@ struct TRaw {
   u32x4_t v[WF == WF_BF16 ? 4 : 1];
 };
 
-// Row block nb (global over the expert-concatenated matrix), k unit kb.
+// Raw-buffer resource word 3 for gfx9 untyped dword access.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// The row blocks nb0 .. nb0+nblk-1 of one tiled matrix (and of its scales)
+// that a workgroup reads, addressed as raw buffers: the base sits in SGPRs,
+// a lane supplies one 32-bit offset and each load adds a uniform offset, so
+// no 64-bit per-lane address is kept per load.  Loads beyond the slab
+// return 0.
 template <int WF>
-__device__ __forceinline__ TRaw<WF> tload(const uint8_t* mat, size_t nb, int K, int kb, int lane) {
+struct Slab {
+  __amdgpu_buffer_rsrc_t w, s;
+  int K;
+  __device__ __forceinline__ Slab(const uint8_t* mat, const uint16_t* sc, size_t nb0, int nblk,
+                                  int K_)
+      : K(K_) {
+    const size_t blk = 16 * row_bytes<WF>(K_);
+    w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(mat + nb0 * blk), 0,
+                                          static_cast<int>(nblk * blk), kRawBufferWord3);
+    if constexpr (WF != WF_BF16) {
+      const size_t sblk = static_cast<size_t>(K_ / 128) * 128;   // bytes of scales per block
+      s = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(sc) + nb0 * sblk), 0,
+          static_cast<int>(nblk * sblk), kRawBufferWord3);
+    }
+  }
+};
+
+// Row block mb of the slab, k unit kb.
+template <int WF>
+__device__ __forceinline__ TRaw<WF> tload(const Slab<WF>& S, int mb, int kb, int lane) {
   TRaw<WF> t;
   if constexpr (WF == WF_BF16) {
-    const size_t frag = nb * static_cast<size_t>(K / 32) + 4 * static_cast<size_t>(kb);
+    const int soff = (mb * (S.K / 32) + 4 * kb) * 1024;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) t.v[f] = ld16(mat + ((frag + f) * 64 + lane) * 16);
+    for (int f = 0; f < 4; ++f)
+      t.v[f] = __builtin_amdgcn_raw_buffer_load_b128(S.w, lane * 16 + f * 1024, soff, 0);
   } else if constexpr (WF == WF_INT4) {
-    t.v[0] = ld16(mat + ((nb * static_cast<size_t>(K / 128) + kb) * 64 + lane) * 16);
+    t.v[0] = __builtin_amdgcn_raw_buffer_load_b128(S.w, lane * 16, (mb * (S.K / 128) + kb) * 1024, 0);
   } else {
-    const u32x2_t d = *reinterpret_cast<const u32x2_t*>(
-        mat + ((nb * static_cast<size_t>(K / 128) + kb) * 64 + lane) * 8);
+    const u32x2_t d =
+        __builtin_amdgcn_raw_buffer_load_b64(S.w, lane * 8, (mb * (S.K / 128) + kb) * 512, 0);
     t.v[0] = u32x4_t{d[0], d[1], 0u, 0u};
   }
   return t;
@@ -407,8 +435,17 @@ __device__ __forceinline__ u32x4_t tdecode(const TRaw<WF>& t, int s, Dq d) {
   }
 }
 
-__device__ __forceinline__ Scales<4> tscales(const uint16_t* sc, size_t nb, int K, int kb, int r) {
-  return load_scales<4>(sc + ((nb * static_cast<size_t>(K / 128) + kb) * 16 + r) * 4, 0);
+// fp16 scales of groups 4 kb .. 4 kb + 3 of row r of block mb.
+template <int WF>
+__device__ __forceinline__ Scales<4> tscales(const Slab<WF>& S, int mb, int kb, int r) {
+  const u32x2_t v =
+      __builtin_amdgcn_raw_buffer_load_b64(S.s, r * 8, (mb * (S.K / 128) + kb) * 128, 0);
+  Scales<4> o;
+  o.s[0] = static_cast<uint16_t>(v[0]);
+  o.s[1] = static_cast<uint16_t>(v[0] >> 16);
+  o.s[2] = static_cast<uint16_t>(v[1]);
+  o.s[3] = static_cast<uint16_t>(v[1] >> 16);
+  return o;
 }
 
 template <int WF>
@@ -439,7 +476,8 @@ __global__ __launch_bounds__(256) void k_gateup_t(
   if (!tile_item(tiles[3 * max_tiles], I / (16 * MB * RG), band, xcd != 0, ti, sl)) return;
   const Tile tl = read_tile(tiles, ti);
   if (tl.rows <= 0) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index as a uniform value (the slab base below must live in SGPRs)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
   const Dq dq = dq_consts<WF>();
   const int kp = wave % KSPLIT, rg = wave / KSPLIT;
@@ -447,6 +485,7 @@ __global__ __launch_bounds__(256) void k_gateup_t(
   const int units = H / 128 / KSPLIT;
   const int ub = kp * units;
   const size_t nb0 = (static_cast<size_t>(tl.e) * I + i0) / 16;
+  const Slab<WF> Sg(wg, sg, nb0, MB, H), Su(wu, su, nb0, MB, H);
 
   const uint16_t* px[NB];
 #pragma unroll
@@ -474,14 +513,14 @@ __global__ __launch_bounds__(256) void k_gateup_t(
     if constexpr (WF != WF_BF16) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        S.sc[mb][0] = tscales(sg, nb0 + mb, H, u, r);
-        S.sc[mb][1] = tscales(su, nb0 + mb, H, u, r);
+        S.sc[mb][0] = tscales(Sg, mb, u, r);
+        S.sc[mb][1] = tscales(Su, mb, u, r);
       }
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      S.raw[mb][0] = tload<WF>(wg, nb0 + mb, H, u, lane);
-      S.raw[mb][1] = tload<WF>(wu, nb0 + mb, H, u, lane);
+      S.raw[mb][0] = tload<WF>(Sg, mb, u, lane);
+      S.raw[mb][1] = tload<WF>(Su, mb, u, lane);
     }
 #pragma unroll
     for (int st = 0; st < 4; ++st)
@@ -583,11 +622,13 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
   if (!tile_item(tiles[3 * max_tiles], H / (64 * MB), band, xcd != 0, ti, sl)) return;
   const Tile tl = read_tile(tiles, ti);
   if (tl.rows <= 0) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index as a uniform value (the slab base below must live in SGPRs)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
   const Dq dq = dq_consts<WF>();
   const int n0 = (sl * 4 + wave) * 16 * MB;
   const size_t nb0 = (static_cast<size_t>(tl.e) * H + n0) / 16;
+  const Slab<WF> Sd(wd, sd, nb0, MB, I);
   const uint16_t* ph[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -607,10 +648,10 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
   auto load = [&](Stage& S, int u) {
     if constexpr (WF != WF_BF16) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) S.sc[mb] = tscales(sd, nb0 + mb, I, u, r);
+      for (int mb = 0; mb < MB; ++mb) S.sc[mb] = tscales(Sd, mb, u, r);
     }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) S.raw[mb] = tload<WF>(wd, nb0 + mb, I, u, lane);
+    for (int mb = 0; mb < MB; ++mb) S.raw[mb] = tload<WF>(Sd, mb, u, lane);
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
@@ -687,12 +728,14 @@ __global__ __launch_bounds__(256) void k_gateup_x(
   if (!tile_item(tiles[3 * max_tiles], I / (64 * MB), band, xcd != 0, ti, sl)) return;
   const Tile tl = read_tile(tiles, ti);
   if (tl.rows <= 0) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index as a uniform value (the slab base below must live in SGPRs)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
   const Dq dq = dq_consts<WF>();
   const int i0 = (sl * 4 + wave) * 16 * MB;
   const int units = H / 128;
   const size_t nb0 = (static_cast<size_t>(tl.e) * I + i0) / 16;
+  const Slab<WF> Sg(wg, sg, nb0, MB, H), Su(wu, su, nb0, MB, H);
 
   XUnit<NB> xu;
   xu.init(x, [&](int R) {
@@ -718,14 +761,14 @@ __global__ __launch_bounds__(256) void k_gateup_x(
     if constexpr (WF != WF_BF16) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        sc[mb][0] = tscales(sg, nb0 + mb, H, u, r);
-        sc[mb][1] = tscales(su, nb0 + mb, H, u, r);
+        sc[mb][0] = tscales(Sg, mb, u, r);
+        sc[mb][1] = tscales(Su, mb, u, r);
       }
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      raw[mb][0] = tload<WF>(wg, nb0 + mb, H, u, lane);
-      raw[mb][1] = tload<WF>(wu, nb0 + mb, H, u, lane);
+      raw[mb][0] = tload<WF>(Sg, mb, u, lane);
+      raw[mb][1] = tload<WF>(Su, mb, u, lane);
     }
     if (u + 1 < units) xu.load(u + 1);
     SCHED_FENCE();
@@ -793,12 +836,14 @@ __global__ __launch_bounds__(256) void k_down_x(const uint16_t* __restrict__ h,
   if (!tile_item(tiles[3 * max_tiles], H / (64 * MB), band, xcd != 0, ti, sl)) return;
   const Tile tl = read_tile(tiles, ti);
   if (tl.rows <= 0) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index as a uniform value (the slab base below must live in SGPRs)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
   const Dq dq = dq_consts<WF>();
   const int n0 = (sl * 4 + wave) * 16 * MB;
   const int units = I / 128;
   const size_t nb0 = (static_cast<size_t>(tl.e) * H + n0) / 16;
+  const Slab<WF> Sd(wd, sd, nb0, MB, I);
 
   XUnit<NB> xu;
   xu.init(h, [&](int R) { return static_cast<size_t>(tl.row0 + min(R, tl.rows - 1)) * I; });
@@ -817,10 +862,10 @@ __global__ __launch_bounds__(256) void k_down_x(const uint16_t* __restrict__ h,
     TRaw<WF> raw[MB];
     if constexpr (WF != WF_BF16) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) sc[mb] = tscales(sd, nb0 + mb, I, u, r);
+      for (int mb = 0; mb < MB; ++mb) sc[mb] = tscales(Sd, mb, u, r);
     }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) raw[mb] = tload<WF>(wd, nb0 + mb, I, u, lane);
+    for (int mb = 0; mb < MB; ++mb) raw[mb] = tload<WF>(Sd, mb, u, lane);
     if (u + 1 < units) xu.load(u + 1);
     SCHED_FENCE();
     const char* buf = xs[u & 1];

@@ -75,7 +75,9 @@ typedef enum {
   MOE_E_WORKSPACE = 7,  /* workspace NULL or smaller than moe_workspace_size() */
   MOE_E_LIMIT = 8,      /* index arithmetic would exceed 2^31                  */
   MOE_E_DEVICE = 9,     /* HIP reported an error while enqueuing               */
-  MOE_E_FLAGS = 10      /* unknown bit in moe_shape.flags                      */
+  MOE_E_FLAGS = 10,     /* unknown bit in moe_shape.flags                      */
+  MOE_E_NONFINITE = 11  /* MOE_F_CHECK_FINITE found a NaN or infinity; caller
+                           outputs were not written                            */
 } moe_status;
 
 typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
@@ -90,6 +92,17 @@ typedef enum { MOE_WF_DENSE = 0, MOE_WF_INT4_G32 = 1, MOE_WF_INT2_G32 = 2 } moe_
 
 /* moe_shape.flags bits. */
 #define MOE_F_TILED_WEIGHTS 0x1u /* expert weights in the tiled layout (moe_tile_experts) */
+/* Non-finite rejection with transactional publication ("Agent Field Notes --
+ * full corpus", AFN-010 "One bank flip is enough: make the whole inference
+ * chunk transactional", section "The publication model": outputs stay
+ * private while work is fallible, finite checks and device status must
+ * pass, then everything is published at one point).  Honoured by moe_route and moe_layer, ignored by the other entry
+ * points: the call computes into the workspace, checks x, the router logits
+ * and (moe_layer) the layer output for NaN / infinity on the device, then
+ * SYNCHRONIZES the stream.  A non-finite value returns MOE_E_NONFINITE with
+ * every caller output untouched; otherwise the results are copied to the
+ * caller outputs (enqueued on the stream) and MOE_OK is returned. */
+#define MOE_F_CHECK_FINITE 0x2u
 
 typedef struct {
   int32_t T;       /* tokens in the batch                        */

@@ -22,11 +22,12 @@ WFMT = {"dense": MOE_WF_DENSE, "int4_g32": MOE_WF_INT4_G32, "int2_g32": MOE_WF_I
 STATUS = {
     0: "MOE_OK", 1: "MOE_E_NULL", 2: "MOE_E_SHAPE", 3: "MOE_E_DTYPE", 4: "MOE_E_FORMAT",
     5: "MOE_E_ALIGN", 6: "MOE_E_ALIAS", 7: "MOE_E_WORKSPACE", 8: "MOE_E_LIMIT",
-    9: "MOE_E_DEVICE", 10: "MOE_E_FLAGS",
+    9: "MOE_E_DEVICE", 10: "MOE_E_FLAGS", 11: "MOE_E_NONFINITE",
 }
 EXPORTS = ("moe_workspace_size", "moe_status_str", "moe_tile_experts", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_layer")
 MOE_F_TILED_WEIGHTS = 0x1
+MOE_F_CHECK_FINITE = 0x2
 
 
 class MoEError(RuntimeError):

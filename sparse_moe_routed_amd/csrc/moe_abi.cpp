@@ -61,6 +61,16 @@ bool make_plan(const moe_shape& s, Plan* p) {
   off = align_up(off + static_cast<size_t>(P) * s.I * act_bytes(s), 256);
   p->y_off = off;
   off = align_up(off + static_cast<size_t>(P) * s.H * act_bytes(s), 256);
+  if (s.flags & MOE_F_CHECK_FINITE) {
+    p->ids_off = off;
+    off = align_up(off + static_cast<size_t>(P) * 4, 256);
+    p->w_off = off;
+    off = align_up(off + static_cast<size_t>(P) * 4, 256);
+    p->out_off = off;
+    off = align_up(off + static_cast<size_t>(T) * s.H * act_bytes(s), 256);
+    p->status_off = off;
+    off = align_up(off + 4, 256);
+  }
   p->total = off;
   return true;
 }
@@ -95,7 +105,7 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 static int check_shape(const moe_shape* s) {
   if (!s) return MOE_E_NULL;
-  if (s->flags & ~MOE_F_TILED_WEIGHTS) return MOE_E_FLAGS;
+  if (s->flags & ~(MOE_F_TILED_WEIGHTS | MOE_F_CHECK_FINITE)) return MOE_E_FLAGS;
   if (s->act != MOE_DT_F32 && s->act != MOE_DT_BF16) return MOE_E_DTYPE;
   if (s->wfmt != MOE_WF_DENSE && s->wfmt != MOE_WF_INT4_G32 && s->wfmt != MOE_WF_INT2_G32)
     return MOE_E_FORMAT;
@@ -193,6 +203,23 @@ static int32_t* ws_tiles(const Plan& pl, void* ws) {
 
 static int device_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_DEVICE; }
 
+// MOE_F_CHECK_FINITE: wait for the enqueued work and read the status word.
+static int finite_status(const Plan& pl, void* ws, hipStream_t st, hipError_t e) {
+  if (e != hipSuccess) return MOE_E_DEVICE;
+  uint32_t host = 0;
+  const uint32_t* dev = reinterpret_cast<const uint32_t*>(static_cast<char*>(ws) + pl.status_off);
+  if (hipMemcpyAsync(&host, dev, sizeof(host), hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return MOE_E_DEVICE;
+  return host ? MOE_E_NONFINITE : MOE_OK;
+}
+
+static hipError_t publish(void* dst, const void* src, size_t bytes, hipStream_t st) {
+  return bytes ? hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st) : hipSuccess;
+}
+
+constexpr uint32_t kBadX = 1u, kBadLogits = 2u, kBadOut = 4u;
+
 }  // namespace moe
 
 using namespace moe;
@@ -220,6 +247,7 @@ const char* moe_status_str(int status) {
     case MOE_E_LIMIT: return "MOE_E_LIMIT: index arithmetic would exceed 2^31";
     case MOE_E_DEVICE: return "MOE_E_DEVICE: HIP error while enqueuing";
     case MOE_E_FLAGS: return "MOE_E_FLAGS: unknown flag bit";
+    case MOE_E_NONFINITE: return "MOE_E_NONFINITE: NaN or infinity found; outputs not written";
     default: return "unknown moe status";
   }
 }
@@ -245,8 +273,25 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router, const
                       {router_bias, router_bias ? s.E * 4u : 0}};
   if (any_alias(outs, 4, ins, 3)) return MOE_E_ALIAS;
   (void)hipGetLastError();
-  return device_status(
-      launch_route(s, pl, x, w_router, router_bias, topk_ids, topk_w, logits, workspace, stream));
+  if (!(s.flags & MOE_F_CHECK_FINITE))
+    return device_status(
+        launch_route(s, pl, x, w_router, router_bias, topk_ids, topk_w, logits, workspace, stream));
+  // private results, checked, then published
+  char* wsb = static_cast<char*>(workspace);
+  int32_t* pids = reinterpret_cast<int32_t*>(wsb + pl.ids_off);
+  float* pw = reinterpret_cast<float*>(wsb + pl.w_off);
+  float* plg = reinterpret_cast<float*>(wsb + pl.logits_off);
+  uint32_t* status = reinterpret_cast<uint32_t*>(wsb + pl.status_off);
+  const bool bf = s.act == MOE_DT_BF16;
+  hipError_t e = launch_zero_status(status, stream);
+  if (e == hipSuccess) e = launch_check_finite(x, static_cast<size_t>(s.T) * s.H, bf, kBadX, status, stream);
+  if (e == hipSuccess) e = launch_route(s, pl, x, w_router, router_bias, pids, pw, plg, workspace, stream);
+  if (e == hipSuccess) e = launch_check_finite(plg, static_cast<size_t>(s.T) * s.E, false, kBadLogits, status, stream);
+  if ((st = finite_status(pl, workspace, stream, e))) return st;
+  e = publish(topk_ids, pids, P * 4, stream);
+  if (e == hipSuccess) e = publish(topk_w, pw, P * 4, stream);
+  if (e == hipSuccess && logits) e = publish(logits, plg, static_cast<size_t>(s.T) * s.E * 4, stream);
+  return device_status(e);
 }
 
 int moe_permute(const moe_shape* shape, const int32_t* topk_ids, const moe_perm* perm,
@@ -415,15 +460,51 @@ int moe_layer(const moe_shape* shape, const void* x, const void* w_router, const
   expert_spans(s, *experts, ins + 4);
   if (any_alias(outs, no, ins, 10)) return MOE_E_ALIAS;
   (void)hipGetLastError();
-  const PermPtrs pp = perm ? perm_ptrs(*perm) : ws_perm(s, pl, workspace);
   int32_t* tiles = ws_tiles(pl, workspace);
-  void* h = static_cast<char*>(workspace) + pl.h_off;
-  void* y = static_cast<char*>(workspace) + pl.y_off;
-  hipError_t e = launch_route(s, pl, x, w_router, router_bias, topk_ids, topk_w, nullptr, workspace,
-                              stream);
-  if (e == hipSuccess) e = launch_permute(s, pl, topk_ids, pp, tiles, workspace, stream);
-  if (e == hipSuccess) e = launch_ffn(s, pl, x, *experts, pp.sorted_pair, tiles, h, y, stream);
-  if (e == hipSuccess) e = launch_combine(s, y, pp.pair_row, topk_w, residual, out, stream);
+  char* wsb = static_cast<char*>(workspace);
+  void* h = wsb + pl.h_off;
+  void* y = wsb + pl.y_off;
+  if (!(s.flags & MOE_F_CHECK_FINITE)) {
+    const PermPtrs pp = perm ? perm_ptrs(*perm) : ws_perm(s, pl, workspace);
+    hipError_t e = launch_route(s, pl, x, w_router, router_bias, topk_ids, topk_w, nullptr,
+                                workspace, stream);
+    if (e == hipSuccess) e = launch_permute(s, pl, topk_ids, pp, tiles, workspace, stream);
+    if (e == hipSuccess) e = launch_ffn(s, pl, x, *experts, pp.sorted_pair, tiles, h, y, stream);
+    if (e == hipSuccess) e = launch_combine(s, y, pp.pair_row, topk_w, residual, out, stream);
+    return device_status(e);
+  }
+  // private results (ids, weights, permutation, output), checked, then published
+  const PermPtrs wp = ws_perm(s, pl, workspace);
+  int32_t* pids = reinterpret_cast<int32_t*>(wsb + pl.ids_off);
+  float* pw = reinterpret_cast<float*>(wsb + pl.w_off);
+  void* pout = wsb + pl.out_off;
+  uint32_t* status = reinterpret_cast<uint32_t*>(wsb + pl.status_off);
+  const bool bf = s.act == MOE_DT_BF16;
+  const size_t TH = static_cast<size_t>(s.T) * s.H;
+  hipError_t e = launch_zero_status(status, stream);
+  if (e == hipSuccess) e = launch_check_finite(x, TH, bf, kBadX, status, stream);
+  if (e == hipSuccess)
+    e = launch_route(s, pl, x, w_router, router_bias, pids, pw, nullptr, workspace, stream);
+  if (e == hipSuccess)
+    e = launch_check_finite(wsb + pl.logits_off, static_cast<size_t>(s.T) * s.E, false, kBadLogits,
+                            status, stream);
+  if (e == hipSuccess) e = launch_permute(s, pl, pids, wp, tiles, workspace, stream);
+  if (e == hipSuccess) e = launch_ffn(s, pl, x, *experts, wp.sorted_pair, tiles, h, y, stream);
+  if (e == hipSuccess) e = launch_combine(s, y, wp.pair_row, pw, residual, pout, stream);
+  if (e == hipSuccess) e = launch_check_finite(pout, TH, bf, kBadOut, status, stream);
+  if ((st = finite_status(pl, workspace, stream, e))) return st;
+  e = publish(out, pout, TH * ab, stream);
+  if (e == hipSuccess) e = publish(topk_ids, pids, P * 4, stream);
+  if (e == hipSuccess) e = publish(topk_w, pw, P * 4, stream);
+  if (e == hipSuccess && perm) {
+    const PermPtrs cp = perm_ptrs(*perm);
+    e = publish(cp.counts, wp.counts, s.E * 4u, stream);
+    if (e == hipSuccess) e = publish(cp.offsets, wp.offsets, (s.E + 1) * 4u, stream);
+    if (e == hipSuccess) e = publish(cp.sorted_pair, wp.sorted_pair, P * 4, stream);
+    if (e == hipSuccess) e = publish(cp.pair_row, wp.pair_row, P * 4, stream);
+    if (e == hipSuccess) e = publish(cp.active, wp.active, s.E * 4u, stream);
+    if (e == hipSuccess) e = publish(cp.n_active, wp.n_active, 4, stream);
+  }
   return device_status(e);
 }
 

@@ -26,6 +26,11 @@ struct Plan {
   size_t tiles_off;       // int32 [3*max_tiles] (expert, row0, rows) + n_tiles
   size_t h_off;           // act [P][I] SwiGLU intermediate
   size_t y_off;           // act [P][H] expert outputs (moe_layer only)
+  // MOE_F_CHECK_FINITE: private results until the status word is clean
+  size_t ids_off;         // int32 [P]
+  size_t w_off;           // float [P]
+  size_t out_off;         // act [T][H] (moe_layer)
+  size_t status_off;      // uint32 status word
   size_t total;
 };
 
@@ -56,6 +61,10 @@ hipError_t launch_ffn(const moe_shape& s, const Plan& pl, const void* x, const m
                       hipStream_t st);
 hipError_t launch_tile_experts(const moe_shape& s, const moe_experts& src, const moe_experts& dst,
                                hipStream_t st);
+hipError_t launch_zero_status(uint32_t* status, hipStream_t st);
+// sets `bit` in *status if any of the n values (bf16 or float32) is NaN/inf
+hipError_t launch_check_finite(const void* src, size_t n, bool bf16, uint32_t bit,
+                               uint32_t* status, hipStream_t st);
 hipError_t launch_combine(const moe_shape& s, const void* y, const int32_t* pair_row,
                           const float* w, const void* residual, void* out, hipStream_t st);
 

@@ -10,9 +10,10 @@ from . import _abi
 class MoELayerBuffers:
     """Outputs, permutation arrays and workspace for a shape, on one device."""
 
-    def __init__(self, T, H, E, I, top_k, act="bf16", wfmt="dense", device="cuda", tiled=False):
-        self.shape = _abi.make_shape(T, H, E, I, top_k, act, wfmt,
-                                     _abi.MOE_F_TILED_WEIGHTS if tiled else 0)
+    def __init__(self, T, H, E, I, top_k, act="bf16", wfmt="dense", device="cuda", tiled=False,
+                 check_finite=False):
+        flags = (_abi.MOE_F_TILED_WEIGHTS if tiled else 0) | (_abi.MOE_F_CHECK_FINITE if check_finite else 0)
+        self.shape = _abi.make_shape(T, H, E, I, top_k, act, wfmt, flags)
         self.T, self.H, self.E, self.I, self.k = T, H, E, I, top_k
         self.act = act
         dt = torch.float32 if act == "f32" else torch.bfloat16

@@ -94,7 +94,7 @@ def _route(s, b, **over):
 @pytest.mark.parametrize("field,value,code", [
     ("H", 100, 2), ("H", 0, 2), ("I", 48, 2), ("E", 2000, 2), ("top_k", 0, 2),
     ("top_k", 600, 2), ("T", -1, 2), ("T", 131073, 2), ("act", 7, 3), ("wfmt", 9, 4),
-    ("flags", 2, 10), ("flags", 0x80000000, 10),
+    ("flags", 4, 10), ("flags", 0x80000000, 10),
 ])
 def test_route_rejects_bad_shape(field, value, code):
     b = bufs()
@@ -190,4 +190,17 @@ def test_tile_experts_validation():
     assert M.moe_tile_experts(shape(), src, src, stream=0, check=False) == 6           # in place
     assert M.moe_tile_experts(shape(I=96), src, dst, stream=0, check=False) == 2
     assert M.moe_tile_experts(shape(), src, None, stream=0, check=False) == 1
+    assert all(v.untouched() for v in b.values())
+
+
+def test_check_finite_flag_workspace():
+    """MOE_F_CHECK_FINITE is a known flag; its private result buffers make
+    the workspace larger."""
+    plain = M.moe_workspace_size(shape())
+    checked = M.moe_workspace_size(shape(flags=M.MOE_F_CHECK_FINITE))
+    P = 8 * 10
+    assert checked >= plain + 2 * P * 4 + 8 * 2560 * 2 + 4
+    b = bufs()
+    st = _route(shape(flags=M.MOE_F_CHECK_FINITE), b, workspace_bytes=checked - 1)
+    assert st == 7
     assert all(v.untouched() for v in b.values())

@@ -309,6 +309,78 @@ def test_fused_equals_staged(name):
         assert torch.equal(ta, tb), name_
 
 
+PERM_NAMES = ("counts", "offsets", "sorted_pair", "pair_row", "active", "n_active")
+
+
+@pytest.mark.parametrize("name", ["bf16_ragged", "int4_small", "decode"])
+def test_check_finite_clean_equals_unchecked(name):
+    """MOE_F_CHECK_FINITE on finite inputs: same bits as without the flag."""
+    case, _ = get(name)
+    cfg = case.cfg
+    res = case.li.x if cfg.residual else None
+    a, b = buffers(cfg), M.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.I, cfg.k, cfg.act, cfg.wfmt,
+                                           device=DEV, check_finite=True)
+    say(f"[check_finite clean {name}]")
+    a.layer(case.li.x, case.li.w_router, case.li.bias, case.ex_gpu, residual=res)
+    b.layer(case.li.x, case.li.w_router, case.li.bias, case.ex_gpu, residual=res)
+    sync()
+    for n in ("out", "topk_ids", "topk_w") + PERM_NAMES:
+        ta, tb = getattr(a, n), getattr(b, n)
+        if ta.dtype == torch.bfloat16:
+            ta, tb = ta.view(torch.int16), tb.view(torch.int16)
+        assert torch.equal(ta, tb), n
+    a.route(case.li.x, case.li.w_router, case.li.bias)
+    b.route(case.li.x, case.li.w_router, case.li.bias)
+    sync()
+    for n in ("topk_ids", "topk_w", "logits"):
+        assert torch.equal(getattr(a, n), getattr(b, n)), n
+
+
+@pytest.mark.parametrize("where", ["x_nan", "x_inf", "router_nan", "expert_inf"])
+def test_check_finite_rejects_and_publishes_nothing(where):
+    """A NaN or infinity anywhere on the path returns MOE_E_NONFINITE and
+    leaves every caller output at its sentinel (the fail-closed publication
+    rule)."""
+    cfg = SMALL["bf16_ragged"]
+    case = make_case(cfg)
+    x, wr = case.li.x.clone(), case.li.w_router.clone()
+    ex = {n: (None if t is None else t.clone()) for n, t in case.li.experts.items()}
+    if where == "x_nan":
+        x[3, 17] = float("nan")
+    elif where == "x_inf":
+        x[0, 0] = float("inf")
+    elif where == "router_nan":
+        wr[5, 100] = float("nan")
+    else:
+        probe = buffers(cfg)
+        probe.route(x, wr, case.li.bias)
+        sync()
+        e0 = int(probe.topk_ids[0, 0].item())
+        ex["gate"][e0, :, :] = float("inf")                  # every row of a selected expert
+    exg = M.make_experts(ex["gate"], ex["up"], ex["down"])
+    b = M.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.I, cfg.k, cfg.act, cfg.wfmt, device=DEV,
+                          check_finite=True)
+    sentinels = {"out": 7.0, "topk_ids": -5, "topk_w": 3.0, "logits": 9.0}
+    for n in PERM_NAMES:
+        sentinels[n] = -7
+    for n, v in sentinels.items():
+        getattr(b, n).fill_(v)
+    sync()
+    say(f"[check_finite reject {where}] moe_layer")
+    with pytest.raises(M.MoEError) as err:
+        b.layer(x, wr, case.li.bias, exg)
+    assert err.value.status == 11
+    if where != "expert_inf":
+        say(f"[check_finite reject {where}] moe_route")
+        with pytest.raises(M.MoEError) as err:
+            b.route(x, wr, case.li.bias)
+        assert err.value.status == 11
+    sync()
+    for n, v in sentinels.items():
+        t = getattr(b, n)
+        assert bool((t == v).all()), f"{n} was written"
+
+
 def test_batch_partition_invariance():
     """Routes of 512 tokens in one call equal those of 8 calls of 64 tokens
     (the replay/decode route-parity requirement), bit for bit."""

@@ -49,6 +49,12 @@ def parse():
                     help="expert weight layout (tiled: converted once at load time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="read this many MiB of scratch between timed steps (evicts L2/MALL with "
+                         "clean lines); each step is then timed on its own and value = tokens / sum "
+                         "of step times")
+    ap.add_argument("--probe-mib", type=int, default=4096,
+                    help="buffer size of the read-bandwidth probe (0: skip)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (PMC calibration)")
     return ap.parse_args()
@@ -203,18 +209,35 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    # one event at every step boundary (plus one after each step when
+    # flushing, so that the flush is outside the step times)
+    ev_beg = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] if args.flush_mib else None
+    scratch = sink = None
+    if args.flush_mib:
+        scratch = torch.zeros(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        M.moe_stream_read(scratch, scratch.numel(), sink)
+        torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t_start.record()
     for i in range(args.steps):
+        ev_beg[i].record()
         step(i, timed_idx=i)
-    t_end.record()
+        if scratch is not None:
+            ev_end[i].record()
+            M.moe_stream_read(scratch, scratch.numel(), sink)
+    ev_beg[args.steps].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    elapsed_ms = t_start.elapsed_time(t_end)
+    if scratch is None:
+        step_ms = np.array([ev_beg[i].elapsed_time(ev_beg[i + 1]) for i in range(args.steps)])
+        elapsed_ms = ev_beg[0].elapsed_time(ev_beg[args.steps])
+    else:
+        step_ms = np.array([ev_beg[i].elapsed_time(ev_end[i]) for i in range(args.steps)])
+        elapsed_ms = float(step_ms.sum())
     ms_per_step = elapsed_ms / args.steps
     tokens_per_s = T * args.steps / (elapsed_ms / 1e3)
+    del scratch, sink
 
     # ---- dominant kernel roofline --------------------------------------------
     gu_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
@@ -240,6 +263,7 @@ def main():
     traffic = traffic_from_profiles(args.workload, digest)
 
     step_bytes = np.mean([sum(layer_bytes(cfg, U[b, l]) for l in range(L)) for b in range(len(xs))])
+    probe = read_probe(M, dev, args.probe_mib) if args.probe_mib else None
 
     # ---- CPU oracle on a bounded sample --------------------------------------
     cpu = None
@@ -269,7 +293,15 @@ def main():
                      "kernel": "k_gateup (grouped gate/up + SwiGLU)",
                      "avg_launch_us": round(avg_ms * 1e3, 3),
                      "algorithmic_bytes_per_launch": round(avg_bytes),
-                     "flops_per_launch": round(avg_flops), "kernel_source_digest": digest},
+                     "flops_per_launch": round(avg_flops), "kernel_source_digest": digest,
+                     "measured_read_GBps": probe,
+                     "frac_of_measured": (round(achieved / probe, 4)
+                                          if probe and bound == "hbm" else None)},
+        "timing": {"mode": ("steps back to back" if not args.flush_mib else
+                            f"{args.flush_mib} MiB scratch read between steps, excluded"),
+                   "step_ms_median": round(float(np.median(step_ms)), 5),
+                   "step_ms_p10": round(float(np.percentile(step_ms, 10)), 5),
+                   "step_ms_p90": round(float(np.percentile(step_ms, 90)), 5)},
         "layer_hbm": {"bytes_per_step": round(step_bytes),
                       "achieved_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
                       "frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -278,6 +310,27 @@ def main():
         "host_wall_s": round(wall, 3),
     }
     print(json.dumps(line))
+
+
+def read_probe(M, dev, mib):
+    """Read bandwidth of the plain streaming probe kernel (moe_stream_read) over
+    a buffer of `mib` MiB: median of 5 timed passes after 2 untimed ones."""
+    import torch
+    n = mib << 20
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        M.moe_stream_read(buf, n, sink)
+    ms = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        M.moe_stream_read(buf, n, sink)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    del buf
+    return round(n / (float(np.median(ms)) / 1e3) / 1e9, 1)
 
 
 def cpu_baseline(cfg, L, layers, xs, budget_s, dev):

@@ -256,6 +256,13 @@ int moe_layer(const moe_shape* shape, const void* x, const void* w_router,
               const moe_perm* perm, void* workspace, size_t workspace_bytes,
               hipStream_t stream);
 
+/* Measurement helper, not part of the layer: streams `bytes` (a non-zero
+ * multiple of 16) from `buf` once with 16-byte loads spread over 2048
+ * workgroups, the read-bandwidth ceiling that the layer's kernels are
+ * compared with.  `sink` is one uint32 the kernel may write (not a result).
+ * buf 16-byte aligned, sink 4-byte aligned and outside buf. */
+int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

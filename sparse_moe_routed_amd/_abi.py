@@ -25,7 +25,8 @@ STATUS = {
     9: "MOE_E_DEVICE", 10: "MOE_E_FLAGS", 11: "MOE_E_NONFINITE",
 }
 EXPORTS = ("moe_workspace_size", "moe_status_str", "moe_tile_experts", "moe_route", "moe_permute",
-           "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_layer")
+           "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_layer",
+           "moe_stream_read")
 MOE_F_TILED_WEIGHTS = 0x1
 MOE_F_CHECK_FINITE = 0x2
 
@@ -78,10 +79,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_ffn_gate_up.argtypes = [P(moe_shape), vp, P(moe_experts), P(moe_perm), vp, vp, sz, vp]
     lib.moe_ffn_down.argtypes = [P(moe_shape), vp, P(moe_experts), vp, vp, sz, vp]
     lib.moe_combine.argtypes = [P(moe_shape), vp, vp, vp, vp, vp, vp]
+    lib.moe_stream_read.argtypes = [vp, sz, vp, vp]
     lib.moe_layer.argtypes = [P(moe_shape), vp, vp, vp, P(moe_experts), vp, vp, vp, vp,
                               P(moe_perm), vp, sz, vp]
     for name in ("moe_tile_experts", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down",
-                 "moe_combine", "moe_layer"):
+                 "moe_combine", "moe_layer", "moe_stream_read"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -192,3 +194,9 @@ def moe_layer(shape, x, w_router, router_bias, experts, residual, out, topk_ids,
                           None if perm is None else ctypes.byref(perm), ptr(workspace),
                           workspace_bytes, stream_handle(stream))
     return _ret(st, "moe_layer", check)
+
+
+def moe_stream_read(buf, nbytes, sink, stream=None, check=True) -> int:
+    """Read-bandwidth probe: stream nbytes of buf once (measurement helper)."""
+    st = load().moe_stream_read(ptr(buf), nbytes, ptr(sink), stream_handle(stream))
+    return _ret(st, "moe_stream_read", check)

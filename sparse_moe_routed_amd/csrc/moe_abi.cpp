@@ -508,4 +508,13 @@ int moe_layer(const moe_shape* shape, const void* x, const void* w_router, const
   return device_status(e);
 }
 
+int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!buf || !sink) return MOE_E_NULL;
+  if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return MOE_E_ALIGN;
+  if (bytes == 0 || bytes % 16 != 0) return MOE_E_SHAPE;
+  if (overlap(Span{buf, bytes}, Span{sink, 4})) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  return device_status(launch_stream_read(buf, bytes, sink, stream));
+}
+
 }  // extern "C"

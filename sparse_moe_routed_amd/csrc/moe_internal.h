@@ -61,6 +61,7 @@ hipError_t launch_ffn(const moe_shape& s, const Plan& pl, const void* x, const m
                       hipStream_t st);
 hipError_t launch_tile_experts(const moe_shape& s, const moe_experts& src, const moe_experts& dst,
                                hipStream_t st);
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_zero_status(uint32_t* status, hipStream_t st);
 // sets `bit` in *status if any of the n values (bf16 or float32) is NaN/inf
 hipError_t launch_check_finite(const void* src, size_t n, bool bf16, uint32_t bit,

@@ -204,3 +204,14 @@ def test_check_finite_flag_workspace():
     st = _route(shape(flags=M.MOE_F_CHECK_FINITE), b, workspace_bytes=checked - 1)
     assert st == 7
     assert all(v.untouched() for v in b.values())
+
+
+def test_stream_read_validation():
+    b = HostBuf(1 << 12)
+    sink = HostBuf(64)
+    assert M.moe_stream_read(None, 16, sink.addr, stream=0, check=False) == 1
+    assert M.moe_stream_read(b.addr, 0, sink.addr, stream=0, check=False) == 2
+    assert M.moe_stream_read(b.addr, 24, sink.addr, stream=0, check=False) == 2
+    assert M.moe_stream_read(b.addr + 8, 16, sink.addr, stream=0, check=False) == 5
+    assert M.moe_stream_read(b.addr, 1024, b.addr + 512, stream=0, check=False) == 6
+    assert b.untouched() and sink.untouched()

@@ -560,3 +560,13 @@ def test_tile_layout_bit_exact(wfmt):
             sa = np_of(src[name + "_scale"])
             sg = np_of(dst[name + "_scale"]).reshape(-1)
             assert np.array_equal(sg, arrange_scales(sa.reshape(-1, K // 32), K)), name + " scales"
+
+
+def test_stream_read_probe():
+    """The read-bandwidth probe runs and leaves its sink alone on zero data
+    (the fold of zeros never equals the magic value)."""
+    buf = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
+    sink = torch.full((1,), 5, dtype=torch.int32, device=DEV)
+    assert M.moe_stream_read(buf, buf.numel(), sink) == 0
+    sync()
+    assert int(sink.item()) == 5

@@ -235,6 +235,14 @@ def test_full_prefill():
     assert c.max() > 10 * c[c > 0].mean()          # Zipf bias skews loads as specified
 
 
+def test_full_prefill_merged():
+    """Eight 4096-token windows in one call (T = 32768), the shape where the
+    grouped GEMMs pass the bf16 ridge; routes for all tokens, outputs for a
+    sample."""
+    ref = _full_layer_check(C3.with_(name="prefill_merged", T=32768), 0, 8, 5)
+    assert int(ref.perm.n_active) == C3.E or ref.perm.counts.max() > 100
+
+
 @pytest.mark.parametrize("layer", [0, 47])
 def test_full_stack_int4_layer(layer):
     _full_layer_check(C4, layer, 12, 2 + layer)

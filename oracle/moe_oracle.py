@@ -67,7 +67,10 @@ R5 low-bit weights are signed symmetric integer codes times an fp16 scale per
 R6 inside an expert segment of the permutation, rows are in ascending pair
    order (hence ascending token order);
 R7 a stacked layer feeds ``x_{l+1} = act_round(x_l + moe_l(x_l))`` where the
-   activation storage type rounds once per layer.
+   activation storage type rounds once per layer;
+R8 route locality is measured on the token sequence t = 0..T-1 of one call:
+   overlap with the previous token, and unions over consecutive blocks of B
+   tokens (the last block may be shorter).
 
 Parity unpinned: last-bit behaviour of exp/silu is not pinned by the pages
 (only by closed forms and library special cases at tolerance level).
@@ -553,3 +556,44 @@ def repeat_fraction(ids: np.ndarray) -> float:
     vals, cnt = np.unique(flat, return_counts=True)
     rep = set(vals[cnt >= 2].tolist())
     return float(np.mean([e in rep for e in flat]))
+
+
+# ----------------------------------------------------------------------------
+# Route locality of a token sequence ([P-019] "Hypothesis H7: DFlash block
+# size must follow I/O cost" and the routing measurements of its "Gate B -
+# trace-only locality": overlap with the previous token, block unions for
+# block sizes 2-5, unique experts per block, per-layer skew, and the routed-
+# byte break-even U_B < 10 tau(B)).  Reading R8: tokens are in sequence
+# order t = 0..T-1; S_t is the set of experts token t selects; a block of
+# size B is tokens bB .. min(T, bB+B)-1 (the last block may be shorter).
+# ----------------------------------------------------------------------------
+
+
+def overlap_with_previous(ids: np.ndarray) -> np.ndarray:
+    """|S_t intersect S_{t-1}| for t >= 1; 0 for t = 0."""
+    ids = np.asarray(ids)
+    out = np.zeros(ids.shape[0], dtype=np.int64)
+    for t in range(1, ids.shape[0]):
+        out[t] = len(set(ids[t].tolist()) & set(ids[t - 1].tolist()))
+    return out
+
+
+def block_unique(ids: np.ndarray, B: int) -> np.ndarray:
+    """|S_bB union ... union S_min(T,bB+B)-1| for every block b."""
+    ids = np.asarray(ids)
+    T = ids.shape[0]
+    return np.array([len(set(ids[b:b + B].reshape(-1).tolist())) for b in range(0, T, B)],
+                    dtype=np.int64)
+
+
+def layer_skew(counts: np.ndarray, k: int, T: int) -> float:
+    """Largest expert load over the mean load per expert (T*k / E)."""
+    counts = np.asarray(counts)
+    return float(counts.max() / (T * k / counts.size))
+
+
+def breakeven_tau(mean_unique: float, k: int) -> float:
+    """Accepted tokens per block at which a block with mean_unique unique
+    experts per layer reads as many routed bytes per accepted token as top-k
+    decoding (the equality case of U_B < k tau(B))."""
+    return mean_unique / k

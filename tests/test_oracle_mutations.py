@@ -158,7 +158,29 @@ def m_payload_bits_bytes(layers, k, H, I, bits):
     return O.param_uses_per_token(layers, k, H, I) * bits / 10
 
 
+def m_overlap_two_back(ids):
+    ids = np.asarray(ids)
+    out = np.zeros(ids.shape[0], dtype=np.int64)
+    for t in range(2, ids.shape[0]):
+        out[t] = len(set(ids[t].tolist()) & set(ids[t - 2].tolist()))
+    return out
+
+
+def m_block_unique_overlapping(ids, B):
+    ids = np.asarray(ids)
+    return np.array([len(set(ids[b:b + B + 1].reshape(-1).tolist()))
+                     for b in range(0, ids.shape[0], B)], dtype=np.int64)
+
+
+def m_block_unique_count_pairs(ids, B):
+    ids = np.asarray(ids)
+    return np.array([ids[b:b + B].size for b in range(0, ids.shape[0], B)], dtype=np.int64)
+
+
 MUTATIONS = [
+    ("overlap_with_previous", m_overlap_two_back),
+    ("block_unique", m_block_unique_overlapping),
+    ("block_unique", m_block_unique_count_pairs),
     ("decode_bf16", m_decode_bf16_shift),
     ("unpack_codes", m_unpack_unsigned),
     ("unpack_codes", m_unpack_high_first),

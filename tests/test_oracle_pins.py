@@ -484,3 +484,53 @@ def test_grouped_stages_compose_to_ffn():
     wg, wu, _ = ex.expert(int(e))
     g, u = wg @ x[t], wu @ x[t]
     np.testing.assert_allclose(A[r], g * scipy.special.expit(g) * u, rtol=1e-13)
+
+
+# ---- route locality (AFN-019 "Hypothesis H7", "Gate B - trace-only locality") ----
+
+def _window_ids(T, k, E, step):
+    """token t selects experts (step*t + j) mod E, j < k"""
+    return np.array([[(step * t + j) % E for j in range(k)] for t in range(T)])
+
+
+def test_pin_locality_closed_forms():
+    T, k, E = 13, 10, 512
+    same = np.tile(np.arange(k), (T, 1))
+    assert list(O.overlap_with_previous(same)) == [0] + [k] * (T - 1)
+    slide = _window_ids(T, k, E, 1)                 # consecutive tokens share k - 1 experts
+    assert list(O.overlap_with_previous(slide)) == [0] + [k - 1] * (T - 1)
+    disjoint = _window_ids(T, k, E, k)              # no expert in common
+    assert list(O.overlap_with_previous(disjoint)) == [0] * T
+    for B in range(1, 6):
+        lens = [min(B, T - b) for b in range(0, T, B)]   # last block ragged (13 tokens)
+        assert list(O.block_unique(same, B)) == [k] * len(lens)
+        assert list(O.block_unique(slide, B)) == [k + n - 1 for n in lens]
+        assert list(O.block_unique(disjoint, B)) == [k * n for n in lens]
+
+
+def test_pin_locality_bitset_bruteforce():
+    """Against an independent bitset/popcount formulation on random routes."""
+    rng = np.random.default_rng(11)
+    for T, k, E in ((7, 3, 9), (17, 5, 23), (1, 4, 4)):
+        ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)])
+        masks = [sum(1 << int(e) for e in row) for row in ids]
+        ov = [0] + [bin(masks[t] & masks[t - 1]).count("1") for t in range(1, T)]
+        assert list(O.overlap_with_previous(ids)) == ov
+        for B in range(1, 6):
+            un = []
+            for b in range(0, T, B):
+                m = 0
+                for t in range(b, min(T, b + B)):
+                    m |= masks[t]
+                un.append(bin(m).count("1"))
+            assert list(O.block_unique(ids, B)) == un
+
+
+def test_pin_breakeven_tau_and_skew():
+    # the page's block-of-five example: 40 unique experts break even at tau = 4
+    assert O.breakeven_tau(PAGE["breakeven_block5_tau4"], 10) == 4
+    assert O.breakeven_tau(PAGE["worstcase_block5"], 10) == 5
+    assert O.layer_skew(np.full(16, 5), k=2, T=40) == 1.0
+    c = np.zeros(16, dtype=np.int64)
+    c[3] = 80
+    assert O.layer_skew(c, k=2, T=40) == 16.0

@@ -203,6 +203,7 @@ def main():
 
     # ---- routing statistics per (batch, layer), untimed ---------------------
     U = np.zeros((len(xs), L), dtype=np.int64)
+    loc = {"overlap": [], "blocks": {B: [] for B in range(1, 6)}, "skew": []}
     for b in range(len(xs)):
         x = xs[b]
         for l, (wr, bias, _, exg) in enumerate(layers):
@@ -210,6 +211,13 @@ def main():
             buf.route(x, wr, bias, logits=False)
             buf.permute()
             U[b, l] = int(buf.n_active.item())
+            ov, blocks = buf.route_locality()
+            loc["overlap"].append(ov[1:].float().mean().item() if T > 1 else 0.0)
+            for B in range(1, 6):
+                full = blocks[B - 1][: T // B]          # full blocks only
+                if full.numel():
+                    loc["blocks"][B].append(full.float().mean().item())
+            loc["skew"].append(int(buf.counts.max().item()) / (T * k / cfg.E))
             buf.ffn_gate_up(x, exg)
             buf.ffn_down(exg)
             buf.combine(residual=x if cfg.residual else None, out=out)
@@ -273,6 +281,23 @@ def main():
     traffic = traffic_from_profiles(args.workload, digest)
 
     step_bytes = np.mean([sum(layer_bytes(cfg, U[b, l]) for l in range(L)) for b in range(len(xs))])
+    # route-locality kernel time (on the last routes)
+    la, lb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    buf.route_locality()
+    la.record()
+    for _ in range(20):
+        buf.route_locality()
+    lb.record()
+    torch.cuda.synchronize()
+    ub = {B: (round(float(np.mean(v)), 3) if v else None) for B, v in loc["blocks"].items()}
+    route_locality = {
+        "over": f"{len(xs)} batches x {L} layers",
+        "mean_overlap_with_previous_token": round(float(np.mean(loc["overlap"])), 3),
+        "unique_experts_per_block": {str(B): v for B, v in ub.items()},
+        "breakeven_tau": {str(B): (round(v / k, 3) if v is not None else None) for B, v in ub.items()},
+        "mean_skew_max_over_mean_load": round(float(np.mean(loc["skew"])), 2),
+        "kernel_us": round(la.elapsed_time(lb) / 20 * 1e3, 2),
+    }
     probe = read_probe(M, dev, args.probe_mib) if args.probe_mib else None
 
     # ---- CPU oracle on a bounded sample --------------------------------------
@@ -316,6 +341,7 @@ def main():
                       "achieved_GBps": round(step_bytes / (ms_per_step / 1e3) / 1e9, 1),
                       "frac": round(step_bytes / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                       "mean_unique_experts_per_layer": round(float(U.mean()), 2)},
+        "route_locality": route_locality,
         "cpu_baseline": cpu,
         "host_wall_s": round(wall, 3),
     }

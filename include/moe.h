@@ -256,6 +256,23 @@ int moe_layer(const moe_shape* shape, const void* x, const void* w_router,
               const moe_perm* perm, void* workspace, size_t workspace_bytes,
               hipStream_t stream);
 
+/* Route locality of the token sequence t = 0..T-1 of one call (AFN-019,
+ * "Hypothesis H7: DFlash block size must follow I/O cost", and its
+ * trace-only locality gate).  With S_t the set {topk_ids[t][j]}:
+ *   overlap_prev[t] = |S_t intersect S_{t-1}|, overlap_prev[0] = 0;
+ *   block_unique[o_B + b] = |S_{bB} union ... union S_{min(T, bB+B) - 1}|
+ *     for B = 1..5 and b < ceil(T/B), with o_1 = 0 and
+ *     o_{B+1} = o_B + ceil(T/B); moe_route_locality_blocks(T) entries.
+ * int32, exact.  topk_ids [T][top_k] rows must hold distinct experts (as
+ * moe_route produces); values are only compared.  overlap_prev [T] and
+ * block_unique are outputs.  Cost per block value O(B^2 top_k^2) compares.
+ * The mean of block_unique over the blocks of size B is U_B; a verifier
+ * block of B tokens reads fewer routed bytes per accepted token than top-k
+ * decoding iff U_B < top_k * tau(B). */
+size_t moe_route_locality_blocks(int32_t T);
+int moe_route_locality(const moe_shape* shape, const int32_t* topk_ids, int32_t* overlap_prev,
+                       int32_t* block_unique, hipStream_t stream);
+
 /* Measurement helper, not part of the layer: streams `bytes` (a non-zero
  * multiple of 16) from `buf` once with 16-byte loads spread over 2048
  * workgroups, the read-bandwidth ceiling that the layer's kernels are

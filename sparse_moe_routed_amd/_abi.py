@@ -26,7 +26,7 @@ STATUS = {
 }
 EXPORTS = ("moe_workspace_size", "moe_status_str", "moe_tile_experts", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_layer",
-           "moe_stream_read")
+           "moe_route_locality_blocks", "moe_route_locality", "moe_stream_read")
 MOE_F_TILED_WEIGHTS = 0x1
 MOE_F_CHECK_FINITE = 0x2
 
@@ -80,10 +80,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_ffn_down.argtypes = [P(moe_shape), vp, P(moe_experts), vp, vp, sz, vp]
     lib.moe_combine.argtypes = [P(moe_shape), vp, vp, vp, vp, vp, vp]
     lib.moe_stream_read.argtypes = [vp, sz, vp, vp]
+    lib.moe_route_locality_blocks.argtypes = [i32]
+    lib.moe_route_locality_blocks.restype = sz
+    lib.moe_route_locality.argtypes = [P(moe_shape), vp, vp, vp, vp]
     lib.moe_layer.argtypes = [P(moe_shape), vp, vp, vp, P(moe_experts), vp, vp, vp, vp,
                               P(moe_perm), vp, sz, vp]
     for name in ("moe_tile_experts", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down",
-                 "moe_combine", "moe_layer", "moe_stream_read"):
+                 "moe_combine", "moe_layer", "moe_route_locality", "moe_stream_read"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -200,3 +203,13 @@ def moe_stream_read(buf, nbytes, sink, stream=None, check=True) -> int:
     """Read-bandwidth probe: stream nbytes of buf once (measurement helper)."""
     st = load().moe_stream_read(ptr(buf), nbytes, ptr(sink), stream_handle(stream))
     return _ret(st, "moe_stream_read", check)
+
+
+def moe_route_locality_blocks(T: int) -> int:
+    return int(load().moe_route_locality_blocks(T))
+
+
+def moe_route_locality(shape, topk_ids, overlap_prev, block_unique, stream=None, check=True) -> int:
+    st = load().moe_route_locality(ctypes.byref(shape), ptr(topk_ids), ptr(overlap_prev),
+                                   ptr(block_unique), stream_handle(stream))
+    return _ret(st, "moe_route_locality", check)

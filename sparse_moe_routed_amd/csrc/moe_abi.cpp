@@ -508,6 +508,26 @@ int moe_layer(const moe_shape* shape, const void* x, const void* w_router, const
   return device_status(e);
 }
 
+size_t moe_route_locality_blocks(int32_t T) {
+  return T <= 0 ? 0 : static_cast<size_t>(locality_blocks(T));
+}
+
+int moe_route_locality(const moe_shape* shape, const int32_t* topk_ids, int32_t* overlap_prev,
+                       int32_t* block_unique, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if ((st = check_ptrs({topk_ids, overlap_prev, block_unique}))) return st;
+  const size_t P = static_cast<size_t>(s.T) * s.top_k;
+  const Span outs[] = {{overlap_prev, static_cast<size_t>(s.T) * 4},
+                       {block_unique, moe_route_locality_blocks(s.T) * 4}};
+  const Span ins[] = {{topk_ids, P * 4}};
+  if (any_alias(outs, 2, ins, 1)) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  return device_status(launch_route_locality(s, topk_ids, overlap_prev, block_unique, stream));
+}
+
 int moe_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
   if (!buf || !sink) return MOE_E_NULL;
   if (!aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return MOE_E_ALIGN;

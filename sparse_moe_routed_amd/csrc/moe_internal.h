@@ -61,6 +61,9 @@ hipError_t launch_ffn(const moe_shape& s, const Plan& pl, const void* x, const m
                       hipStream_t st);
 hipError_t launch_tile_experts(const moe_shape& s, const moe_experts& src, const moe_experts& dst,
                                hipStream_t st);
+int locality_blocks(int T);   // sum over B = 1..5 of ceil(T / B)
+hipError_t launch_route_locality(const moe_shape& s, const int32_t* ids, int32_t* overlap,
+                                 int32_t* block_unique, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_zero_status(uint32_t* status, hipStream_t st);
 // sets `bit` in *status if any of the n values (bf16 or float32) is NaN/inf

@@ -45,6 +45,22 @@ class MoELayerBuffers:
         return _abi.moe_permute(self.shape, self.topk_ids if topk_ids is None else topk_ids,
                                 self.perm, self.workspace, self.ws_bytes, stream)
 
+    def route_locality(self, topk_ids=None, stream=None):
+        """(overlap_prev [T], [block_unique for B = 1..5]) as device tensors."""
+        if not hasattr(self, "overlap_prev"):
+            dev = self.topk_ids.device
+            self.overlap_prev = torch.empty(self.T, dtype=torch.int32, device=dev)
+            self.block_unique = torch.empty(max(_abi.moe_route_locality_blocks(self.T), 1),
+                                            dtype=torch.int32, device=dev)
+        _abi.moe_route_locality(self.shape, self.topk_ids if topk_ids is None else topk_ids,
+                                self.overlap_prev, self.block_unique, stream)
+        parts, o = [], 0
+        for B in range(1, 6):
+            nb = (self.T + B - 1) // B
+            parts.append(self.block_unique[o:o + nb])
+            o += nb
+        return self.overlap_prev, parts
+
     def grouped_ffn(self, x, experts, perm=None, stream=None):
         return _abi.moe_grouped_ffn(self.shape, x, experts, self.perm if perm is None else perm,
                                     self.y, self.workspace, self.ws_bytes, stream)

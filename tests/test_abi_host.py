@@ -215,3 +215,16 @@ def test_stream_read_validation():
     assert M.moe_stream_read(b.addr + 8, 16, sink.addr, stream=0, check=False) == 5
     assert M.moe_stream_read(b.addr, 1024, b.addr + 512, stream=0, check=False) == 6
     assert b.untouched() and sink.untouched()
+
+
+def test_route_locality_blocks_and_validation():
+    assert M.moe_route_locality_blocks(13) == 13 + 7 + 5 + 4 + 3
+    assert M.moe_route_locality_blocks(1) == 5
+    assert M.moe_route_locality_blocks(0) == 0
+    b = bufs()
+    s = shape()
+    assert M.moe_route_locality(s, None, b["ids"].addr, b["w"].addr, stream=0, check=False) == 1
+    assert M.moe_route_locality(s, b["ids"].addr, b["ids"].addr, b["w"].addr, stream=0,
+                                check=False) == 6
+    assert M.moe_route_locality(shape(T=0), None, None, None, stream=0, check=False) == 0
+    assert all(v.untouched() for v in b.values())

@@ -578,3 +578,31 @@ def test_stream_read_probe():
     assert M.moe_stream_read(buf, buf.numel(), sink) == 0
     sync()
     assert int(sink.item()) == 5
+
+
+def _locality_check(ids_np, E):
+    T, k = ids_np.shape
+    buf = M.MoELayerBuffers(T, 256, E, 64, k, "bf16", "dense", device=DEV)
+    ov, blocks = buf.route_locality(topk_ids=i32(ids_np))
+    sync()
+    assert np.array_equal(ov.cpu().numpy(), O.overlap_with_previous(ids_np))
+    for B in range(1, 6):
+        assert np.array_equal(blocks[B - 1].cpu().numpy(), O.block_unique(ids_np, B)), B
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 10, 512), (2, 10, 512), (13, 10, 512), (37, 7, 100),
+                                   (200, 32, 1024), (64, 1, 3), (300, 10, 16)])
+def test_route_locality_random(T, k, E):
+    """Seeded random routes with distinct experts per token, bit-exact."""
+    rng = np.random.default_rng(1000 + T + k)
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int32)
+    say(f"[locality T={T} k={k} E={E}]")
+    _locality_check(ids, E)
+
+
+@pytest.mark.parametrize("name", ["decode", "int2_small", "prefill_chunked"])
+def test_route_locality_oracle_routes(name):
+    """The oracle's routes of a workload fed to the kernel (teacher forcing)."""
+    case, ref = get(name)
+    say(f"[locality {name}] oracle routes")
+    _locality_check(ref.ids.astype(np.int32), case.cfg.E)

@@ -606,3 +606,51 @@ def test_route_locality_oracle_routes(name):
     case, ref = get(name)
     say(f"[locality {name}] oracle routes")
     _locality_check(ref.ids.astype(np.int32), case.cfg.E)
+
+
+@pytest.mark.parametrize("name,layout", [("decode", "tiled"), ("int4_small", "tiled"),
+                                         ("prefill_chunked", "row")])
+def test_layer_hip_graph_replay(name, layout):
+    """The staged layer (route, permute, gate/up, down, combine) captured in a
+    HIP graph: every replay, with eager work and synchronizations between
+    replays, equals the eager result bit for bit (no memset nodes)."""
+    case, _ = get(name)
+    cfg = case.cfg
+    tiled = layout == "tiled"
+    res = case.li.x if cfg.residual else None
+    ex = case.experts(tiled)
+    eager = buffers(cfg, tiled)
+    eager.route(case.li.x, case.li.w_router, case.li.bias)
+    eager.permute()
+    eager.ffn_gate_up(case.li.x, ex)
+    eager.ffn_down(ex)
+    eager.combine(residual=res)
+    sync()
+    g_buf = buffers(cfg, tiled)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    say(f"[graph {name} {layout}] capture")
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            g_buf.route(case.li.x, case.li.w_router, case.li.bias, stream=s)
+            g_buf.permute(stream=s)
+            g_buf.ffn_gate_up(case.li.x, ex, stream=s)
+            g_buf.ffn_down(ex, stream=s)
+            g_buf.combine(residual=res, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    sync()
+    for rep in range(4):
+        g_buf.out.fill_(0)
+        g_buf.topk_ids.fill_(-1)
+        junk = torch.randn(1 << 20, device=DEV).sum()           # eager work between replays
+        sync()
+        graph.replay()
+        sync()
+        say(f"[graph {name} {layout}] replay {rep}")
+        assert torch.equal(g_buf.out.view(torch.int16) if g_buf.out.dtype == torch.bfloat16
+                           else g_buf.out, eager.out.view(torch.int16)
+                           if eager.out.dtype == torch.bfloat16 else eager.out)
+        assert torch.equal(g_buf.topk_ids, eager.topk_ids)
+        assert torch.equal(g_buf.sorted_pair, eager.sorted_pair)
+        del junk

@@ -63,6 +63,9 @@ def parse():
                     help="skip the HIP-graph replay measurement (extra field `graph`)")
     ap.add_argument("--probe-mib", type=int, default=4096,
                     help="buffer size of the read-bandwidth probe (0: skip)")
+    ap.add_argument("--no-offload", action="store_true",
+                    help="skip the host-resident expert measurement (extra field `offload`)")
+    ap.add_argument("--offload-steps", type=int, default=20)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (PMC calibration)")
     return ap.parse_args()
@@ -94,12 +97,16 @@ def layer_bytes(cfg, U):
     return U * rec + cfg.E * cfg.H * act + 2 * cfg.T * cfg.H * act
 
 
+# the files that define the grouped FFN kernels and how they are compiled
+DIGEST_FILES = ("sparse_moe_routed_amd/csrc/k_ffn.hip", "sparse_moe_routed_amd/csrc/moe_device.h",
+                "sparse_moe_routed_amd/csrc/moe_internal.h", "sparse_moe_routed_amd/build.py")
+
+
 def kernel_source_digest():
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_moe_routed_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+    for f in DIGEST_FILES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
     return h.hexdigest()[:16]
 
 
@@ -302,6 +309,7 @@ def main():
         "kernel_us": round(la.elapsed_time(lb) / 20 * 1e3, 2),
     }
     probe = read_probe(M, dev, args.probe_mib) if args.probe_mib else None
+    off = None if args.no_offload else offload(M, torch, dev, cfg, layers, xs, buf, args.offload_steps)
 
     # ---- CPU oracle on a bounded sample --------------------------------------
     cpu = None
@@ -346,6 +354,7 @@ def main():
                       "mean_unique_experts_per_layer": round(float(U.mean()), 2)},
         "route_locality": route_locality,
         "graph": graph,
+        "offload": off,
         "cpu_baseline": cpu,
         "host_wall_s": round(wall, 3),
     }
@@ -391,6 +400,106 @@ def graph_replay(torch, buf, layers, xs, acts, cfg, L, steps):
         return {"ms_per_step": round(ms, 5), "tokens_per_s": round(cfg.T / (ms / 1e3), 1),
                 "graphs": len(xs)}
     except Exception as e:   # capture is optional; the eager numbers stand
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
+def offload(M, torch, dev, cfg, layers, xs, buf, steps):
+    """Host-resident expert records: layer 0's records in pinned host memory,
+    a device array of the same layout as the staging target.  One step is one
+    layer: route -> permute -> stage the exact active union over PCIe (the GPU
+    reads the pinned records itself; the active set never reaches the host)
+    -> gate/up -> down -> combine.  `split`: gate/up records staged first and
+    down on a second stream while gate/up computes; `serial`: one staging
+    launch before the FFN.  `full_extent` copies every expert's records (the
+    sequential layer-extent mode for prefill) with the staging kernel and
+    with a plain host-to-device copy; the crossover is the unique-expert count
+    at which the exact union costs as much as the full extent."""
+    try:
+        wr, bias, ex, _ = layers[0]
+        names = ("gate", "up", "down", "gate_scale", "up_scale", "down_scale")
+        host = {n: (None if ex[n] is None else
+                    torch.empty(ex[n].shape, dtype=ex[n].dtype, pin_memory=True)) for n in names}
+        for n in names:
+            if ex[n] is not None:
+                host[n].copy_(ex[n])
+        dst = {n: (None if ex[n] is None else torch.empty_like(ex[n])) for n in names}
+        src_s = M.make_experts(*(host[n] for n in names))
+        dst_s = M.make_experts(*(dst[n] for n in names))
+        rec = sum(t.numel() * t.element_size() for t in ex.values() if t is not None) / cfg.E
+        cur, side = torch.cuda.current_stream(), torch.cuda.Stream()
+        res_of = (lambda x: x) if cfg.residual else (lambda x: None)
+
+        def one(x, split):
+            buf.route(x, wr, bias, logits=False)
+            buf.permute()
+            if split:
+                buf.stage_experts(src_s, dst_s, parts=M.MOE_STAGE_GATE_UP)
+                side.wait_stream(cur)
+                buf.stage_experts(src_s, dst_s, parts=M.MOE_STAGE_DOWN, stream=side)
+                buf.ffn_gate_up(x, dst_s)
+                cur.wait_stream(side)
+            else:
+                buf.stage_experts(src_s, dst_s)
+                buf.ffn_gate_up(x, dst_s)
+            buf.ffn_down(dst_s)
+            buf.combine(residual=res_of(x))
+
+        def timed(split):
+            for i in range(2):
+                one(xs[i % len(xs)], split)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(steps):
+                one(xs[i % len(xs)], split)
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / steps
+
+        U = []
+        for i in range(min(steps, len(xs))):
+            buf.route(xs[i], wr, bias, logits=False)
+            buf.permute()
+            U.append(int(buf.n_active.item()))
+        u_mean = float(np.mean([U[i % len(U)] for i in range(steps)]))
+        ms_split, ms_serial = timed(True), timed(False)
+        staged = u_mean * rec
+
+        # full layer extent: every expert active
+        all_active = torch.arange(cfg.E, dtype=torch.int32, device=dev)
+        n_all = torch.full((1,), cfg.E, dtype=torch.int32, device=dev)
+        allp = M.make_perm(buf.counts, buf.offsets, buf.sorted_pair, buf.pair_row, all_active, n_all)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        M.moe_stage_experts(buf.shape, src_s, dst_s, allp)
+        torch.cuda.synchronize()
+        a.record()
+        M.moe_stage_experts(buf.shape, src_s, dst_s, allp)
+        b.record()
+        torch.cuda.synchronize()
+        full_kernel = cfg.E * rec / (a.elapsed_time(b) / 1e3) / 1e9
+        a.record()
+        for n in names:
+            if ex[n] is not None:
+                dst[n].copy_(host[n], non_blocking=True)
+        b.record()
+        torch.cuda.synchronize()
+        full_copy = cfg.E * rec / (a.elapsed_time(b) / 1e3) / 1e9
+        sel = staged / (ms_split / 1e3) / 1e9
+        del host, dst
+        return {"records": "layer 0 expert records in pinned host memory; one step = one layer",
+                "record_bytes_per_expert": round(rec), "mean_unique_experts": round(u_mean, 2),
+                "staged_bytes_per_step": round(staged),
+                "split": {"ms_per_step": round(ms_split, 4),
+                          "tokens_per_s": round(cfg.T / (ms_split / 1e3), 1),
+                          "staged_GBps": round(sel, 2)},
+                "serial": {"ms_per_step": round(ms_serial, 4),
+                           "tokens_per_s": round(cfg.T / (ms_serial / 1e3), 1),
+                           "staged_GBps": round(staged / (ms_serial / 1e3) / 1e9, 2)},
+                "full_extent": {"bytes": round(cfg.E * rec),
+                                "stage_kernel_GBps": round(full_kernel, 2),
+                                "host_to_device_copy_GBps": round(full_copy, 2)},
+                "crossover_unique_experts": round(cfg.E * sel / max(full_kernel, full_copy), 1)}
+    except Exception as e:   # optional measurement; the resident numbers stand
         return {"error": f"{type(e).__name__}: {e}"}
 
 

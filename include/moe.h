@@ -76,8 +76,10 @@ typedef enum {
   MOE_E_LIMIT = 8,      /* index arithmetic would exceed 2^31                  */
   MOE_E_DEVICE = 9,     /* HIP reported an error while enqueuing               */
   MOE_E_FLAGS = 10,     /* unknown bit in moe_shape.flags                      */
-  MOE_E_NONFINITE = 11  /* MOE_F_CHECK_FINITE found a NaN or infinity; caller
+  MOE_E_NONFINITE = 11, /* MOE_F_CHECK_FINITE found a NaN or infinity; caller
                            outputs were not written                            */
+  MOE_E_MEMORY = 12     /* a source buffer is not memory the device can read
+                           (e.g. pageable host memory)                         */
 } moe_status;
 
 typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
@@ -255,6 +257,27 @@ int moe_layer(const moe_shape* shape, const void* x, const void* w_router,
               const void* residual, void* out, int32_t* topk_ids, float* topk_w,
               const moe_perm* perm, void* workspace, size_t workspace_bytes,
               hipStream_t stream);
+
+/* Stage the active experts' records into device memory (AFN-019,
+ * "Hypothesis H5": a block reads the deduplicated union of its routes;
+ * "Why overlap alone cannot defeat the byte roofline": exact bytes first).
+ * For a = 0 .. *perm->n_active - 1 and e = perm->active[a], copies the
+ * records of expert e selected by `parts` (MOE_STAGE_GATE_UP: gate and up
+ * with their scales; MOE_STAGE_DOWN: down with its scale) from `src` to the
+ * same expert positions of `dst`; other experts' regions of dst are not
+ * written.  Gate and up are needed together and down only after them, so a
+ * caller may stage down on a second stream while gate/up runs (the pages'
+ * component split).  src and dst have the same layout (row-major, or tiled
+ * when shape->flags has MOE_F_TILED_WEIGHTS); dst is device memory.  src may
+ * be pinned host memory (hipHostMalloc, torch pin_memory) or device memory:
+ * the GPU reads it directly, so the active set never goes to the host.  One
+ * kernel launch.  MOE_E_FLAGS if parts is 0 or has an unknown bit;
+ * MOE_E_MEMORY if a src buffer is not device-readable or a dst buffer is not
+ * device memory. */
+#define MOE_STAGE_GATE_UP 0x1u
+#define MOE_STAGE_DOWN 0x2u
+int moe_stage_experts(const moe_shape* shape, const moe_experts* src, const moe_experts* dst,
+                      const moe_perm* perm, uint32_t parts, hipStream_t stream);
 
 /* Route locality of the token sequence t = 0..T-1 of one call (AFN-019,
  * "Hypothesis H7: DFlash block size must follow I/O cost", and its

@@ -22,13 +22,16 @@ WFMT = {"dense": MOE_WF_DENSE, "int4_g32": MOE_WF_INT4_G32, "int2_g32": MOE_WF_I
 STATUS = {
     0: "MOE_OK", 1: "MOE_E_NULL", 2: "MOE_E_SHAPE", 3: "MOE_E_DTYPE", 4: "MOE_E_FORMAT",
     5: "MOE_E_ALIGN", 6: "MOE_E_ALIAS", 7: "MOE_E_WORKSPACE", 8: "MOE_E_LIMIT",
-    9: "MOE_E_DEVICE", 10: "MOE_E_FLAGS", 11: "MOE_E_NONFINITE",
+    9: "MOE_E_DEVICE", 10: "MOE_E_FLAGS", 11: "MOE_E_NONFINITE", 12: "MOE_E_MEMORY",
 }
 EXPORTS = ("moe_workspace_size", "moe_status_str", "moe_tile_experts", "moe_route", "moe_permute",
            "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_layer",
-           "moe_route_locality_blocks", "moe_route_locality", "moe_stream_read")
+           "moe_stage_experts", "moe_route_locality_blocks", "moe_route_locality",
+           "moe_stream_read")
 MOE_F_TILED_WEIGHTS = 0x1
 MOE_F_CHECK_FINITE = 0x2
+MOE_STAGE_GATE_UP = 0x1
+MOE_STAGE_DOWN = 0x2
 
 
 class MoEError(RuntimeError):
@@ -83,10 +86,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_route_locality_blocks.argtypes = [i32]
     lib.moe_route_locality_blocks.restype = sz
     lib.moe_route_locality.argtypes = [P(moe_shape), vp, vp, vp, vp]
+    lib.moe_stage_experts.argtypes = [P(moe_shape), P(moe_experts), P(moe_experts), P(moe_perm),
+                                      ctypes.c_uint32, vp]
     lib.moe_layer.argtypes = [P(moe_shape), vp, vp, vp, P(moe_experts), vp, vp, vp, vp,
                               P(moe_perm), vp, sz, vp]
     for name in ("moe_tile_experts", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down",
-                 "moe_combine", "moe_layer", "moe_route_locality", "moe_stream_read"):
+                 "moe_combine", "moe_layer", "moe_route_locality", "moe_stage_experts",
+                 "moe_stream_read"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -213,3 +219,12 @@ def moe_route_locality(shape, topk_ids, overlap_prev, block_unique, stream=None,
     st = load().moe_route_locality(ctypes.byref(shape), ptr(topk_ids), ptr(overlap_prev),
                                    ptr(block_unique), stream_handle(stream))
     return _ret(st, "moe_route_locality", check)
+
+
+def moe_stage_experts(shape, src, dst, perm, parts=None, stream=None, check=True) -> int:
+    parts = MOE_STAGE_GATE_UP | MOE_STAGE_DOWN if parts is None else parts
+    st = load().moe_stage_experts(ctypes.byref(shape), None if src is None else ctypes.byref(src),
+                                  None if dst is None else ctypes.byref(dst),
+                                  None if perm is None else ctypes.byref(perm), parts,
+                                  stream_handle(stream))
+    return _ret(st, "moe_stage_experts", check)

@@ -248,6 +248,7 @@ const char* moe_status_str(int status) {
     case MOE_E_DEVICE: return "MOE_E_DEVICE: HIP error while enqueuing";
     case MOE_E_FLAGS: return "MOE_E_FLAGS: unknown flag bit";
     case MOE_E_NONFINITE: return "MOE_E_NONFINITE: NaN or infinity found; outputs not written";
+    case MOE_E_MEMORY: return "MOE_E_MEMORY: a source buffer is not device-readable memory";
     default: return "unknown moe status";
   }
 }
@@ -506,6 +507,55 @@ int moe_layer(const moe_shape* shape, const void* x, const void* w_router, const
     if (e == hipSuccess) e = publish(cp.n_active, wp.n_active, 4, stream);
   }
   return device_status(e);
+}
+
+// Device-usable address of a buffer the kernel will read: device memory as
+// is, pinned host memory through its device mapping; nullptr otherwise.
+static const char* device_readable(const void* p) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  if (a.type == hipMemoryTypeDevice) return static_cast<const char*>(p);
+  if (a.type == hipMemoryTypeHost && a.devicePointer && a.hostPointer)
+    return static_cast<const char*>(a.devicePointer) +
+           (static_cast<const char*>(p) - static_cast<const char*>(a.hostPointer));
+  return nullptr;
+}
+
+int moe_stage_experts(const moe_shape* shape, const moe_experts* src, const moe_experts* dst,
+                      const moe_perm* perm, uint32_t parts, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  if (parts == 0 || (parts & ~(MOE_STAGE_GATE_UP | MOE_STAGE_DOWN))) return MOE_E_FLAGS;
+  const moe_shape& s = *shape;
+  if ((st = check_experts(s, src)) || (st = check_experts(s, dst)) || (st = check_perm(perm))) return st;
+  Span sp[6], dp[6], pp[6];
+  expert_spans(s, *src, sp);
+  expert_spans(s, *dst, dp);
+  perm_spans(s, *perm, pp);
+  if (any_alias(dp, 6, sp, 6) || any_alias(dp, 6, pp, 6)) return MOE_E_ALIAS;
+  StagePieces pc;
+  const size_t E = static_cast<size_t>(s.E);
+  for (int m = 0; m < kStagePieces; ++m) {
+    pc.src[m] = nullptr;
+    pc.dst[m] = static_cast<char*>(const_cast<void*>(dp[m].p));
+    pc.bytes[m] = sp[m].n / E;
+    // pieces 0, 1, 3, 4 are gate, up and their scales; 2 and 5 are down's
+    const bool down = m == 2 || m == 5;
+    if (!sp[m].p || !(parts & (down ? MOE_STAGE_DOWN : MOE_STAGE_GATE_UP))) continue;
+    if (pc.bytes[m] % 16 != 0) return MOE_E_SHAPE;
+    pc.src[m] = device_readable(sp[m].p);
+    if (!pc.src[m]) return MOE_E_MEMORY;
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, dp[m].p) != hipSuccess || a.type != hipMemoryTypeDevice) {
+      (void)hipGetLastError();
+      return MOE_E_MEMORY;
+    }
+  }
+  (void)hipGetLastError();
+  return device_status(launch_stage_experts(s, pc, perm->active, perm->n_active, stream));
 }
 
 size_t moe_route_locality_blocks(int32_t T) {

@@ -64,6 +64,17 @@ hipError_t launch_tile_experts(const moe_shape& s, const moe_experts& src, const
 int locality_blocks(int T);   // sum over B = 1..5 of ceil(T / B)
 hipError_t launch_route_locality(const moe_shape& s, const int32_t* ids, int32_t* overlap,
                                  int32_t* block_unique, hipStream_t st);
+// Per-expert byte pieces of one expert record set (gate, up, down and their
+// scales): source and destination bases (device-usable addresses) and bytes
+// per expert; a null source skips the piece.
+constexpr int kStagePieces = 6;
+struct StagePieces {
+  const char* src[kStagePieces];
+  char* dst[kStagePieces];
+  size_t bytes[kStagePieces];
+};
+hipError_t launch_stage_experts(const moe_shape& s, const StagePieces& pc, const int32_t* active,
+                                const int32_t* n_active, hipStream_t st);
 hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t st);
 hipError_t launch_zero_status(uint32_t* status, hipStream_t st);
 // sets `bit` in *status if any of the n values (bf16 or float32) is NaN/inf

@@ -45,6 +45,12 @@ class MoELayerBuffers:
         return _abi.moe_permute(self.shape, self.topk_ids if topk_ids is None else topk_ids,
                                 self.perm, self.workspace, self.ws_bytes, stream)
 
+    def stage_experts(self, src, dst, parts=None, stream=None):
+        """Copy the records of this call's active experts (the permutation
+        already built by permute()) from `src` to `dst` (moe_experts structs;
+        src may be pinned host memory); `parts` selects gate/up and/or down."""
+        return _abi.moe_stage_experts(self.shape, src, dst, self.perm, parts, stream)
+
     def route_locality(self, topk_ids=None, stream=None):
         """(overlap_prev [T], [block_unique for B = 1..5]) as device tensors."""
         if not hasattr(self, "overlap_prev"):

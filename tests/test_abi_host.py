@@ -228,3 +228,22 @@ def test_route_locality_blocks_and_validation():
                                 check=False) == 6
     assert M.moe_route_locality(shape(T=0), None, None, None, stream=0, check=False) == 0
     assert all(v.untouched() for v in b.values())
+
+
+def test_stage_experts_validation():
+    b = bufs()
+    src = M.make_experts(b["g"].addr, b["u"].addr, b["d"].addr)
+    dst = M.make_experts(b["gs"].addr, b["us"].addr, b["ds"].addr)
+    pm = M.make_perm(*(b[n].addr for n in ("ids", "w", "logits", "res", "y", "x")))
+    s = shape(E=4, top_k=2, H=128, I=32)       # records fit the 64 KiB buffers
+    assert M.moe_stage_experts(s, None, dst, pm, stream=0, check=False) == 1
+    assert M.moe_stage_experts(s, src, dst, None, stream=0, check=False) == 1
+    assert M.moe_stage_experts(s, src, src, pm, stream=0, check=False) == 6            # in place
+    assert M.moe_stage_experts(shape(flags=4), src, dst, pm, stream=0, check=False) == 10
+    assert M.moe_stage_experts(s, src, dst, pm, parts=0, stream=0, check=False) == 10
+    assert M.moe_stage_experts(s, src, dst, pm, parts=4, stream=0, check=False) == 10
+    odd = M.make_experts(b["g"].addr + 8, b["u"].addr, b["d"].addr)
+    assert M.moe_stage_experts(s, odd, dst, pm, stream=0, check=False) == 5
+    # pageable host memory is not device-readable: rejected before any launch
+    assert M.moe_stage_experts(s, src, dst, pm, stream=0, check=False) == 12
+    assert all(v.untouched() for v in b.values())

@@ -654,3 +654,95 @@ def test_layer_hip_graph_replay(name, layout):
         assert torch.equal(g_buf.topk_ids, eager.topk_ids)
         assert torch.equal(g_buf.sorted_pair, eager.sorted_pair)
         del junk
+
+
+STAGE_CASES = [("int4_small", "tiled", "pinned", False), ("int2_small", "tiled", "pinned", True),
+               ("bf16_ragged", "row", "pinned", True), ("int4_many_rows", "row", "device", False)]
+EXPERT_PIECES = ("gate", "up", "down", "gate_scale", "up_scale", "down_scale")
+
+
+@pytest.mark.parametrize("name,layout,where,split", STAGE_CASES)
+def test_stage_experts(name, layout, where, split):
+    """moe_stage_experts copies exactly the active experts' records (from
+    pinned host or device memory), leaves every other expert's region as it
+    was, and the layer run on the staged records equals the layer run on the
+    resident ones bit for bit.  With `split`, gate/up is staged first (down
+    regions still untouched) and down on a second stream while gate/up runs."""
+    case, _ = get(name)
+    cfg = case.cfg
+    tiled = layout == "tiled"
+    src_t = case.tiled_keep if tiled else case.li.experts
+    src_t = {n: (None if src_t.get(n) is None else
+                 (src_t[n].cpu().pin_memory() if where == "pinned" else src_t[n].clone()))
+             for n in EXPERT_PIECES}
+    dst_t = {n: (None if t is None else torch.empty_like(t, device=DEV)) for n, t in src_t.items()}
+    for t in dst_t.values():
+        if t is not None:
+            t.view(torch.uint8).fill_(0x5A)
+    src = M.make_experts(*(src_t[n] for n in EXPERT_PIECES))
+    dst = M.make_experts(*(dst_t[n] for n in EXPERT_PIECES))
+    ex = case.experts(tiled)
+    res = case.li.x if cfg.residual else None
+    b = buffers(cfg, tiled)
+    b.route(case.li.x, case.li.w_router, case.li.bias)
+    b.permute()
+    say(f"[stage {name} {layout} {where} split={split}] stage")
+    if split:
+        b.stage_experts(src, dst, parts=M.MOE_STAGE_GATE_UP)
+        sync()
+        for n in ("down", "down_scale"):
+            if dst_t[n] is not None:
+                assert bool((dst_t[n].view(torch.uint8) == 0x5A).all()), f"{n} written by gate/up stage"
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        b.stage_experts(src, dst, parts=M.MOE_STAGE_DOWN, stream=side)
+    else:
+        b.stage_experts(src, dst)
+    sync()
+    n_act = int(b.n_active.item())
+    active = set(b.active[:n_act].cpu().tolist())
+    assert active == set(np.nonzero(b.counts.cpu().numpy())[0].tolist())
+    for n in EXPERT_PIECES:
+        if src_t[n] is None:
+            continue
+        s8 = src_t[n].view(torch.uint8).reshape(cfg.E, -1).cpu()
+        d8 = dst_t[n].view(torch.uint8).reshape(cfg.E, -1).cpu()
+        for e in range(cfg.E):
+            if e in active:
+                assert torch.equal(d8[e], s8[e]), f"{n}: expert {e} not copied"
+            else:
+                assert bool((d8[e] == 0x5A).all()), f"{n}: inactive expert {e} written"
+    say(f"[stage {name} {layout} {where} split={split}] layer on staged records")
+    b.ffn_gate_up(case.li.x, dst)
+    b.ffn_down(dst)
+    b.combine(residual=res)
+    staged = b.out.clone()
+    b.ffn_gate_up(case.li.x, ex)
+    b.ffn_down(ex)
+    b.combine(residual=res)
+    sync()
+    assert torch.equal(staged.view(torch.int16), b.out.view(torch.int16))
+
+
+def test_stage_experts_none_active_and_pageable():
+    """n_active = 0 writes nothing; pageable host memory is rejected with
+    MOE_E_MEMORY before any launch."""
+    case, _ = get("int4_small")
+    cfg = case.cfg
+    src_t = {n: case.li.experts.get(n) for n in EXPERT_PIECES}
+    dst_t = {n: (None if t is None else torch.empty_like(t)) for n, t in src_t.items()}
+    for t in dst_t.values():
+        if t is not None:
+            t.view(torch.uint8).fill_(0x5A)
+    b = buffers(cfg)
+    b.route(case.li.x, case.li.w_router, case.li.bias)
+    b.permute()
+    b.n_active.fill_(0)
+    dst = M.make_experts(*(dst_t[n] for n in EXPERT_PIECES))
+    b.stage_experts(M.make_experts(*(src_t[n] for n in EXPERT_PIECES)), dst)
+    sync()
+    assert all(bool((t.view(torch.uint8) == 0x5A).all()) for t in dst_t.values() if t is not None)
+    pageable = {n: (None if t is None else t.cpu()) for n, t in src_t.items()}
+    st = M.moe_stage_experts(b.shape, M.make_experts(*(pageable[n] for n in EXPERT_PIECES)), dst,
+                             b.perm, check=False)
+    assert st == 12

@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--no-offload", action="store_true",
                     help="skip the host-resident expert measurement (extra field `offload`)")
     ap.add_argument("--offload-steps", type=int, default=20)
+    ap.add_argument("--no-fused", action="store_true",
+                    help="skip the fused gate/up -> down measurement (extra field `fused_waves`)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (PMC calibration)")
     return ap.parse_args()
@@ -98,7 +100,8 @@ def layer_bytes(cfg, U):
 
 
 # the files that define the grouped FFN kernels and how they are compiled
-DIGEST_FILES = ("sparse_moe_routed_amd/csrc/k_ffn.hip", "sparse_moe_routed_amd/csrc/moe_device.h",
+DIGEST_FILES = ("sparse_moe_routed_amd/csrc/k_ffn.hip", "sparse_moe_routed_amd/csrc/ffn_tiled.h",
+                "sparse_moe_routed_amd/csrc/moe_device.h",
                 "sparse_moe_routed_amd/csrc/moe_internal.h", "sparse_moe_routed_amd/build.py")
 
 
@@ -310,6 +313,7 @@ def main():
     }
     probe = read_probe(M, dev, args.probe_mib) if args.probe_mib else None
     off = None if args.no_offload else offload(M, torch, dev, cfg, layers, xs, buf, args.offload_steps)
+    fw = None if (args.no_fused or not tiled or T * k > 16384) else fused_waves(M, torch, dev, cfg, layers, xs)
 
     # ---- CPU oracle on a bounded sample --------------------------------------
     cpu = None
@@ -355,6 +359,7 @@ def main():
         "route_locality": route_locality,
         "graph": graph,
         "offload": off,
+        "fused_waves": fw,
         "cpu_baseline": cpu,
         "host_wall_s": round(wall, 3),
     }
@@ -500,6 +505,71 @@ def offload(M, torch, dev, cfg, layers, xs, buf, steps):
                                 "host_to_device_copy_GBps": round(full_copy, 2)},
                 "crossover_unique_experts": round(cfg.E * sel / max(full_kernel, full_copy), 1)}
     except Exception as e:   # optional measurement; the resident numbers stand
+        return {"error": f"{type(e).__name__}: {e}"}
+
+
+def fused_waves(M, torch, dev, cfg, layers, xs, reps=50):
+    """The fused gate/up -> down kernel (moe_ffn_fused) next to the two-kernel
+    FFN on layer 0 of the workload: FFN time per wave width (1, 2, 4 tiles and
+    all), the whole layer with MOE_F_FUSED_FFN against the default layer, and
+    the wave completion profile read from the kernel's per-item clock (for
+    each wave, the last item's gate/up and down completion, from the first
+    item's start)."""
+    try:
+        wr, bias, _, exg = layers[0]
+        mk = lambda fused: M.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.I, cfg.k, cfg.act, cfg.wfmt,
+                                             device=dev, tiled=True, fused=fused)
+        b0, b1 = mk(False), mk(True)
+        res = (lambda x: x) if cfg.residual else (lambda x: None)
+
+        def timeit(fn):
+            for i in range(5):
+                fn(i)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(reps):
+                fn(i)
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / reps * 1e3
+
+        lay0 = timeit(lambda i: b0.layer(xs[i % len(xs)], wr, bias, exg, residual=res(xs[i % len(xs)])))
+        lay1 = timeit(lambda i: b1.layer(xs[i % len(xs)], wr, bias, exg, residual=res(xs[i % len(xs)])))
+        x = xs[0]
+        for b in (b0, b1):
+            b.route(x, wr, bias, logits=False)
+            b.permute()
+        two = timeit(lambda i: (b0.ffn_gate_up(x, exg), b0.ffn_down(exg)))
+        widths = {"1": 1, "2": 2, "4": 4, "all": 0}
+        fused = {n: round(timeit(lambda i: b1.ffn_fused(x, exg, wave_tiles=w)), 2) for n, w in widths.items()}
+        khz = M.moe_device_clock_khz()
+        S = cfg.I // 64
+        cap = M.moe_ffn_fused_items(b1.shape)
+        clock = torch.zeros(3 * cap, dtype=torch.int64, device=dev)
+        prof = {}
+        for n, w in widths.items():
+            clock.zero_()
+            b1.ffn_fused(x, exg, wave_tiles=w, item_clock=clock)
+            torch.cuda.synchronize()
+            c = clock.view(-1, 3).cpu().numpy()
+            c = c[c[:, 0] > 0]
+            per = (w if w else len(c) // S) * S
+            wave = np.arange(len(c)) // per
+            t0 = c[:, 0].min()
+            gu = np.array([c[wave == v, 1].max() for v in np.unique(wave)]) - t0
+            dn = np.array([c[wave == v, 2].max() for v in np.unique(wave)]) - t0
+            us = 1e3 / khz
+            prof[n] = {"waves": int(wave.max() + 1), "items": int(len(c)),
+                       "gate_up_done_us_first_median_last": [round(float(v * us), 2) for v in
+                                                             (gu.min(), np.median(gu), gu.max())],
+                       "down_done_us_first_median_last": [round(float(v * us), 2) for v in
+                                                          (dn.min(), np.median(dn), dn.max())]}
+        del b0, b1, clock
+        return {"layer_us": {"two_kernel": round(lay0, 2), "fused": round(lay1, 2)},
+                "ffn_us": {"two_kernel": round(two, 2), "fused_by_wave_tiles": fused},
+                "wave_completion": prof, "clock_khz": khz}
+    except Exception as e:   # optional measurement
         return {"error": f"{type(e).__name__}: {e}"}
 
 

@@ -105,6 +105,15 @@ typedef enum { MOE_WF_DENSE = 0, MOE_WF_INT4_G32 = 1, MOE_WF_INT2_G32 = 2 } moe_
  * every caller output untouched; otherwise the results are copied to the
  * caller outputs (enqueued on the stream) and MOE_OK is returned. */
 #define MOE_F_CHECK_FINITE 0x2u
+/* Fused expert FFN (AFN-019, "Hypothesis H4": gate/up -> down as component
+ * waves, no barrier between them; see moe_ffn_fused).  Requires
+ * MOE_F_TILED_WEIGHTS (MOE_E_FLAGS otherwise) and T * top_k <= 16384
+ * (MOE_E_LIMIT otherwise: the workspace then holds (I/64) float32 partial
+ * results per pair and feature).  moe_layer runs the FFN as moe_ffn_fused
+ * with one wave of all tiles and adds the partial results in its combine
+ * (y is not formed); moe_ffn_fused requires the flag; the other entry
+ * points ignore it. */
+#define MOE_F_FUSED_FFN 0x4u
 
 typedef struct {
   int32_t T;       /* tokens in the batch                        */
@@ -238,6 +247,36 @@ int moe_ffn_gate_up(const moe_shape* shape, const void* x,
 int moe_ffn_down(const moe_shape* shape, const void* h,
                  const moe_experts* experts, void* y, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);
+
+/* The grouped SwiGLU experts (same y as moe_grouped_ffn, up to float
+ * rounding order) as one kernel of component waves (AFN-019, "Hypothesis
+ * H4": gate+up first, down as soon as the intermediate exists, waves of 2, 4
+ * or all experts, separate result slots).  Work item = (tile, slice of 64
+ * intermediate columns): one workgroup computes the SwiGLU intermediate of
+ * its tile rows for those 64 columns (bf16, in LDS) and at once its share of
+ * the down projection, a float32 partial y_s[row][0..H) for slice s; no
+ * workgroup waits for another.  y[r] = bf16(sum over s ascending of
+ * y_s[r]).  Items are numbered in waves of `wave_tiles` consecutive tiles of
+ * the plan (0: one wave of all tiles), slice-major inside a wave; with
+ * T <= 16 each active expert is exactly one tile.  shape->flags must hold
+ * MOE_F_TILED_WEIGHTS | MOE_F_FUSED_FFN (MOE_E_FLAGS otherwise);
+ * wave_tiles < 0 is MOE_E_SHAPE.  perm as for moe_grouped_ffn.
+ * item_clock: NULL, or uint64 [3 * moe_ffn_fused_items(shape)] (output): for
+ * item i < n_tiles * (I/64) (i = wave * W * S + slice * nt + tile-in-wave,
+ * S = I/64, nt the tiles in that wave), the device wall clock
+ * (moe_device_clock_khz) at the item's start, after its gate/up and after its
+ * down; entries of items past the last tile are not written. */
+int moe_ffn_fused(const moe_shape* shape, const void* x, const moe_experts* experts,
+                  const moe_perm* perm, void* y, int32_t wave_tiles, uint64_t* item_clock,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Capacity in items of moe_ffn_fused's item_clock (max tiles * I/64) for a
+ * valid shape with MOE_F_FUSED_FFN; 0 otherwise.  Host-only. */
+size_t moe_ffn_fused_items(const moe_shape* shape);
+
+/* Rate of the device wall clock of the current device in kHz (ticks per
+ * millisecond), for item_clock. */
+int moe_device_clock_khz(int32_t* khz);
 
 /* Route-rank-order combine: out[t][n] = residual[t][n] +
  * sum_{j=0}^{top_k-1} topk_w[t][j] * y[pair_row[t*top_k+j]][n], accumulated

@@ -25,11 +25,13 @@ STATUS = {
     9: "MOE_E_DEVICE", 10: "MOE_E_FLAGS", 11: "MOE_E_NONFINITE", 12: "MOE_E_MEMORY",
 }
 EXPORTS = ("moe_workspace_size", "moe_status_str", "moe_tile_experts", "moe_route", "moe_permute",
-           "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_combine", "moe_layer",
+           "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_ffn_fused",
+           "moe_ffn_fused_items", "moe_device_clock_khz", "moe_combine", "moe_layer",
            "moe_stage_experts", "moe_route_locality_blocks", "moe_route_locality",
            "moe_stream_read")
 MOE_F_TILED_WEIGHTS = 0x1
 MOE_F_CHECK_FINITE = 0x2
+MOE_F_FUSED_FFN = 0x4
 MOE_STAGE_GATE_UP = 0x1
 MOE_STAGE_DOWN = 0x2
 
@@ -82,6 +84,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_ffn_gate_up.argtypes = [P(moe_shape), vp, P(moe_experts), P(moe_perm), vp, vp, sz, vp]
     lib.moe_ffn_down.argtypes = [P(moe_shape), vp, P(moe_experts), vp, vp, sz, vp]
     lib.moe_combine.argtypes = [P(moe_shape), vp, vp, vp, vp, vp, vp]
+    lib.moe_ffn_fused.argtypes = [P(moe_shape), vp, P(moe_experts), P(moe_perm), vp, i32, vp, vp,
+                                  sz, vp]
+    lib.moe_ffn_fused_items.argtypes = [P(moe_shape)]
+    lib.moe_ffn_fused_items.restype = sz
+    lib.moe_device_clock_khz.argtypes = [P(ctypes.c_int32)]
     lib.moe_stream_read.argtypes = [vp, sz, vp, vp]
     lib.moe_route_locality_blocks.argtypes = [i32]
     lib.moe_route_locality_blocks.restype = sz
@@ -90,9 +97,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                       ctypes.c_uint32, vp]
     lib.moe_layer.argtypes = [P(moe_shape), vp, vp, vp, P(moe_experts), vp, vp, vp, vp,
                               P(moe_perm), vp, sz, vp]
-    for name in ("moe_tile_experts", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down",
-                 "moe_combine", "moe_layer", "moe_route_locality", "moe_stage_experts",
-                 "moe_stream_read"):
+    for name in ("moe_tile_experts", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_ffn_gate_up",
+                 "moe_ffn_down", "moe_ffn_fused", "moe_device_clock_khz", "moe_combine", "moe_layer",
+                 "moe_route_locality", "moe_stage_experts", "moe_stream_read"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -187,6 +194,26 @@ def moe_ffn_down(shape, h, experts, y, workspace, workspace_bytes, stream=None, 
                              None if experts is None else ctypes.byref(experts), ptr(y),
                              ptr(workspace), workspace_bytes, stream_handle(stream))
     return _ret(st, "moe_ffn_down", check)
+
+
+def moe_ffn_fused(shape, x, experts, perm, y, wave_tiles, item_clock, workspace, workspace_bytes,
+                  stream=None, check=True) -> int:
+    st = load().moe_ffn_fused(ctypes.byref(shape), ptr(x),
+                              None if experts is None else ctypes.byref(experts),
+                              None if perm is None else ctypes.byref(perm), ptr(y), wave_tiles,
+                              ptr(item_clock), ptr(workspace), workspace_bytes, stream_handle(stream))
+    return _ret(st, "moe_ffn_fused", check)
+
+
+def moe_ffn_fused_items(shape) -> int:
+    return int(load().moe_ffn_fused_items(ctypes.byref(shape)))
+
+
+def moe_device_clock_khz(check=True) -> int:
+    khz = ctypes.c_int32(0)
+    st = load().moe_device_clock_khz(ctypes.byref(khz))
+    _ret(st, "moe_device_clock_khz", check)
+    return int(khz.value)
 
 
 def moe_combine(shape, y, pair_row, topk_w, residual, out, stream=None, check=True) -> int:

@@ -22,17 +22,11 @@
 // Low-bit weights: one MFMA per group of 32 codes (codes -> exact bf16
 // integers), the float32 group partial is multiplied by the fp16 scale and
 // accumulated in float32.
+#include "ffn_tiled.h"
 #include "moe_device.h"
 #include "moe_internal.h"
 
 namespace moe {
-
-enum { WF_BF16 = 0, WF_INT4 = 1, WF_INT2 = 2 };
-
-template <int WF>
-__device__ __forceinline__ size_t row_bytes(int K) {
-  return WF == WF_BF16 ? static_cast<size_t>(K) * 2 : (WF == WF_INT4 ? K / 2 : K / 4);
-}
 
 // Raw weight bits of one 32-wide k chunk starting at kk for lane chunk q:
 // bf16 -> 16 bytes (8 weights), int4 -> 4 bytes (8 codes), int2 -> 2 bytes.
@@ -73,13 +67,6 @@ __device__ __forceinline__ u32x4_t decode_raw(typename Raw<WF>::type v) {
   }
 }
 
-// fp16 scales of groups g .. g+U-1 of one weight row (U = 1 or 4; 4 requires
-// g % 4 == 0, so the 8-byte load is aligned).
-template <int U>
-struct Scales {
-  uint16_t s[U];
-};
-
 template <int U>
 __device__ __forceinline__ Scales<U> load_scales(const uint16_t* row, int g) {
   Scales<U> r;
@@ -94,45 +81,6 @@ __device__ __forceinline__ Scales<U> load_scales(const uint16_t* row, int g) {
     for (int u = 0; u < U; ++u) r.s[u] = row[g + u];
   }
   return r;
-}
-
-struct Tile {
-  int e, row0, rows;
-};
-
-// Keeps the compiler from interleaving a k unit's loads with its MFMAs: left
-// alone it reuses a few registers for successive loads and waits on each, so
-// one unit pays the memory latency several times over.
-#define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
-
-__device__ __forceinline__ Tile read_tile(const int32_t* tiles, int t) {
-  return Tile{tiles[3 * t], tiles[3 * t + 1], tiles[3 * t + 2]};
-}
-
-// Work item (tile, weight slice) of a 1-D tiled-FFN grid whose size is a
-// multiple of 8.  Items are numbered in bands of `band` tiles, slice-major
-// inside a band, so neighbouring items read the same weight slice of one
-// expert for consecutive token tiles.  With `xcd` set, each run of
-// neighbouring items goes to workgroups of a single XCD (workgroups are
-// handed to the 8 XCDs round-robin by linear id), so the slice that the
-// tiles of a hot expert share is fetched into that XCD's L2 once.
-__device__ __forceinline__ bool tile_item(int n_tiles, int nslices, int band, bool xcd, int& tile,
-                                          int& slice) {
-  const int n = n_tiles * nslices;
-  int L = static_cast<int>(blockIdx.x);
-  if (xcd) {
-    const int per = (n + 7) >> 3;
-    const int j = L >> 3;
-    if (j >= per) return false;
-    L = (L & 7) * per + j;
-  }
-  if (L >= n) return false;
-  const int b0 = L / (band * nslices) * band;
-  const int nt = min(band, n_tiles - b0);
-  const int idx = L - b0 * nslices;
-  slice = idx / nt;
-  tile = b0 + idx % nt;
-  return true;
 }
 
 // gate/up + SwiGLU.  32 intermediate rows (two 16-row MFMA blocks) of gate and
@@ -358,100 +306,6 @@ __global__ __launch_bounds__(256) void k_down(const uint16_t* __restrict__ h,
         if (rr < tl.rows) y[static_cast<size_t>(tl.row0 + rr) * H + n] = f32_to_bf16(acc[mb][b][j]);
       }
   }
-}
-
-// ---------------------------------------------------------------------------
-// Tiled weights (MOE_F_TILED_WEIGHTS).  The unit of the k loop is 128 k = 4
-// MFMA chunks; for one 16-row block a lane fetches, per unit, 4 x 16 B (bf16:
-// four consecutive 1 KB fragments), 16 B (int4) or 8 B (int2), plus 8 B of
-// scales, so every load instruction of a wave reads one contiguous block.
-// ---------------------------------------------------------------------------
-template <int WF>
-struct TRaw {
-  u32x4_t v[WF == WF_BF16 ? 4 : 1];
-};
-
-// Raw-buffer resource word 3 for gfx9 untyped dword access.
-constexpr int kRawBufferWord3 = 0x00020000;
-
-// The row blocks nb0 .. nb0+nblk-1 of one tiled matrix (and of its scales)
-// that a workgroup reads, addressed as raw buffers: the base sits in SGPRs,
-// a lane supplies one 32-bit offset and each load adds a uniform offset, so
-// no 64-bit per-lane address is kept per load.  Loads beyond the slab
-// return 0.
-template <int WF>
-struct Slab {
-  __amdgpu_buffer_rsrc_t w, s;
-  int K;
-  __device__ __forceinline__ Slab(const uint8_t* mat, const uint16_t* sc, size_t nb0, int nblk,
-                                  int K_)
-      : K(K_) {
-    const size_t blk = 16 * row_bytes<WF>(K_);
-    w = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(mat + nb0 * blk), 0,
-                                          static_cast<int>(nblk * blk), kRawBufferWord3);
-    if constexpr (WF != WF_BF16) {
-      const size_t sblk = static_cast<size_t>(K_ / 128) * 128;   // bytes of scales per block
-      s = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(reinterpret_cast<const uint8_t*>(sc) + nb0 * sblk), 0,
-          static_cast<int>(nblk * sblk), kRawBufferWord3);
-    }
-  }
-};
-
-// Row block mb of the slab, k unit kb.
-template <int WF>
-__device__ __forceinline__ TRaw<WF> tload(const Slab<WF>& S, int mb, int kb, int lane) {
-  TRaw<WF> t;
-  if constexpr (WF == WF_BF16) {
-    const int soff = (mb * (S.K / 32) + 4 * kb) * 1024;
-#pragma unroll
-    for (int f = 0; f < 4; ++f)
-      t.v[f] = __builtin_amdgcn_raw_buffer_load_b128(S.w, lane * 16 + f * 1024, soff, 0);
-  } else if constexpr (WF == WF_INT4) {
-    t.v[0] = __builtin_amdgcn_raw_buffer_load_b128(S.w, lane * 16, (mb * (S.K / 128) + kb) * 1024, 0);
-  } else {
-    const u32x2_t d =
-        __builtin_amdgcn_raw_buffer_load_b64(S.w, lane * 8, (mb * (S.K / 128) + kb) * 512, 0);
-    t.v[0] = u32x4_t{d[0], d[1], 0u, 0u};
-  }
-  return t;
-}
-
-template <int WF>
-__device__ __forceinline__ Dq dq_consts() {
-  if constexpr (WF == WF_BF16) return Dq{0u, 0u};   // unused
-  else return Dq{in_vgpr(WF == WF_INT4 ? 0x000F000Fu : 0x00030003u), in_vgpr(0x43004300u)};
-}
-
-template <int WF>
-__device__ __forceinline__ u32x4_t tdecode(const TRaw<WF>& t, int s, Dq d) {
-  if constexpr (WF == WF_BF16) {
-    return t.v[s];
-  } else if constexpr (WF == WF_INT4) {
-    return dequant_int4_tiled(t.v[0][s], d);
-  } else {
-    const uint32_t w = t.v[0][s >> 1];
-    return (s & 1) ? dequant_int2_tiled<1>(w, d) : dequant_int2_tiled<0>(w, d);
-  }
-}
-
-// fp16 scales of groups 4 kb .. 4 kb + 3 of row r of block mb.
-template <int WF>
-__device__ __forceinline__ Scales<4> tscales(const Slab<WF>& S, int mb, int kb, int r) {
-  const u32x2_t v =
-      __builtin_amdgcn_raw_buffer_load_b64(S.s, r * 8, (mb * (S.K / 128) + kb) * 128, 0);
-  Scales<4> o;
-  o.s[0] = static_cast<uint16_t>(v[0]);
-  o.s[1] = static_cast<uint16_t>(v[0] >> 16);
-  o.s[2] = static_cast<uint16_t>(v[1]);
-  o.s[3] = static_cast<uint16_t>(v[1] >> 16);
-  return o;
-}
-
-template <int WF>
-__device__ __forceinline__ u32x4_t neg_offset_fragment() {
-  const uint32_t c = (WF == WF_INT4) ? kNegOffset4 : kNegOffset2;
-  return u32x4_t{c, c, c, c};
 }
 
 // gate/up + SwiGLU on tiled weights.  A wave owns MB 16-row blocks of gate

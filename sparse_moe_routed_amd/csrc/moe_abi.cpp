@@ -36,6 +36,9 @@ static int plan_nb(const moe_shape& s) {
   return 4;
 }
 
+// MOE_F_FUSED_FFN: pairs whose float32 partial results the workspace holds
+constexpr int64_t kFusedMaxPairs = 16384;
+
 static int64_t plan_max_tiles(const moe_shape& s) {
   const int64_t P = static_cast<int64_t>(s.T) * s.top_k;
   return P / (16 * plan_nb(s)) + std::min<int64_t>(s.E, P);
@@ -71,6 +74,10 @@ bool make_plan(const moe_shape& s, Plan* p) {
     p->status_off = off;
     off = align_up(off + 4, 256);
   }
+  if (s.flags & MOE_F_FUSED_FFN) {
+    p->part_off = off;
+    off = align_up(off + static_cast<size_t>(fused_slices(s)) * P * s.H * sizeof(float), 256);
+  }
   p->total = off;
   return true;
 }
@@ -105,7 +112,8 @@ static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 static int check_shape(const moe_shape* s) {
   if (!s) return MOE_E_NULL;
-  if (s->flags & ~(MOE_F_TILED_WEIGHTS | MOE_F_CHECK_FINITE)) return MOE_E_FLAGS;
+  if (s->flags & ~(MOE_F_TILED_WEIGHTS | MOE_F_CHECK_FINITE | MOE_F_FUSED_FFN)) return MOE_E_FLAGS;
+  if ((s->flags & MOE_F_FUSED_FFN) && !(s->flags & MOE_F_TILED_WEIGHTS)) return MOE_E_FLAGS;
   if (s->act != MOE_DT_F32 && s->act != MOE_DT_BF16) return MOE_E_DTYPE;
   if (s->wfmt != MOE_WF_DENSE && s->wfmt != MOE_WF_INT4_G32 && s->wfmt != MOE_WF_INT2_G32)
     return MOE_E_FORMAT;
@@ -122,6 +130,7 @@ static int check_shape(const moe_shape* s) {
   if (T * s->top_k >= (int64_t{1} << 31)) return MOE_E_LIMIT;
   if (T * std::max(s->E, s->H) >= (int64_t{1} << 31)) return MOE_E_LIMIT;
   if (plan_max_tiles(*s) > 65535) return MOE_E_LIMIT;   // FFN grid y dimension
+  if ((s->flags & MOE_F_FUSED_FFN) && T * s->top_k > kFusedMaxPairs) return MOE_E_LIMIT;
   return MOE_OK;
 }
 
@@ -220,6 +229,27 @@ static hipError_t publish(void* dst, const void* src, size_t bytes, hipStream_t 
 
 constexpr uint32_t kBadX = 1u, kBadLogits = 2u, kBadOut = 4u;
 
+// The expert FFN and the combine of moe_layer: gate/up, down, combine of y;
+// or, with MOE_F_FUSED_FFN, the fused kernel and the combine of its partial
+// results.
+static hipError_t ffn_and_combine(const moe_shape& s, const Plan& pl, const void* x,
+                                  const moe_experts& ex, const PermPtrs& pp, const int32_t* tiles,
+                                  const float* w, const void* residual, void* out, void* ws,
+                                  hipStream_t st) {
+  char* wsb = static_cast<char*>(ws);
+  if (s.flags & MOE_F_FUSED_FFN) {
+    float* part = reinterpret_cast<float*>(wsb + pl.part_off);
+    hipError_t e = launch_ffn_fused(s, pl, x, ex, pp.sorted_pair, tiles, part, 0, nullptr, st);
+    if (e == hipSuccess) e = launch_combine_parts(s, part, pp.pair_row, w, residual, out, st);
+    return e;
+  }
+  void* h = wsb + pl.h_off;
+  void* y = wsb + pl.y_off;
+  hipError_t e = launch_ffn(s, pl, x, ex, pp.sorted_pair, tiles, h, y, st);
+  if (e == hipSuccess) e = launch_combine(s, y, pp.pair_row, w, residual, out, st);
+  return e;
+}
+
 }  // namespace moe
 
 using namespace moe;
@@ -246,7 +276,7 @@ const char* moe_status_str(int status) {
     case MOE_E_WORKSPACE: return "MOE_E_WORKSPACE: workspace missing or too small";
     case MOE_E_LIMIT: return "MOE_E_LIMIT: index arithmetic would exceed 2^31";
     case MOE_E_DEVICE: return "MOE_E_DEVICE: HIP error while enqueuing";
-    case MOE_E_FLAGS: return "MOE_E_FLAGS: unknown flag bit";
+    case MOE_E_FLAGS: return "MOE_E_FLAGS: unknown flag bit or unsupported flag combination";
     case MOE_E_NONFINITE: return "MOE_E_NONFINITE: NaN or infinity found; outputs not written";
     case MOE_E_MEMORY: return "MOE_E_MEMORY: a source buffer is not device-readable memory";
     default: return "unknown moe status";
@@ -391,6 +421,60 @@ int moe_ffn_down(const moe_shape* shape, const void* h, const moe_experts* exper
   return device_status(launch_down(s, pl, h, *experts, ws_tiles(pl, workspace), y, stream));
 }
 
+int moe_ffn_fused(const moe_shape* shape, const void* x, const moe_experts* experts,
+                  const moe_perm* perm, void* y, int32_t wave_tiles, uint64_t* item_clock,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const moe_shape& s = *shape;
+  if (!(s.flags & MOE_F_FUSED_FFN)) return MOE_E_FLAGS;
+  if (wave_tiles < 0) return MOE_E_SHAPE;
+  if (s.T == 0) return MOE_OK;
+  if ((st = check_ptrs({x, y}))) return st;
+  if ((st = check_opt_ptr(item_clock))) return st;
+  if ((st = check_experts(s, experts))) return st;
+  if ((st = check_perm(perm))) return st;
+  Plan pl;
+  make_plan(s, &pl);
+  if ((st = check_ws(pl, workspace, workspace_bytes))) return st;
+  const size_t P = static_cast<size_t>(s.T) * s.top_k, ab = act_bytes(s);
+  Span ins[13];
+  ins[0] = {x, static_cast<size_t>(s.T) * s.H * ab};
+  expert_spans(s, *experts, ins + 1);
+  perm_spans(s, *perm, ins + 7);
+  const size_t items = static_cast<size_t>(pl.max_tiles) * fused_slices(s);
+  const Span outs[] = {{y, P * s.H * ab},
+                       {workspace, pl.total},
+                       {item_clock, item_clock ? 3 * items * sizeof(uint64_t) : 0}};
+  if (any_alias(outs, 3, ins, 13)) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  int32_t* tiles = ws_tiles(pl, workspace);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.part_off);
+  hipError_t e = launch_plan_tiles(s, pl, perm_ptrs(*perm), tiles, stream);
+  if (e == hipSuccess)
+    e = launch_ffn_fused(s, pl, x, *experts, perm->sorted_pair, tiles, part, wave_tiles, item_clock,
+                         stream);
+  if (e == hipSuccess) e = launch_reduce_parts(s, part, y, stream);
+  return device_status(e);
+}
+
+size_t moe_ffn_fused_items(const moe_shape* shape) {
+  if (check_shape(shape) != MOE_OK || !(shape->flags & MOE_F_FUSED_FFN)) return 0;
+  return static_cast<size_t>(plan_max_tiles(*shape)) * fused_slices(*shape);
+}
+
+int moe_device_clock_khz(int32_t* khz) {
+  if (!khz) return MOE_E_NULL;
+  int dev = 0, rate = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&rate, hipDeviceAttributeWallClockRate, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return MOE_E_DEVICE;
+  }
+  *khz = rate;
+  return MOE_OK;
+}
+
 int moe_tile_experts(const moe_shape* shape, const moe_experts* src, const moe_experts* dst,
                      hipStream_t stream) {
   int st = check_shape(shape);
@@ -463,15 +547,12 @@ int moe_layer(const moe_shape* shape, const void* x, const void* w_router, const
   (void)hipGetLastError();
   int32_t* tiles = ws_tiles(pl, workspace);
   char* wsb = static_cast<char*>(workspace);
-  void* h = wsb + pl.h_off;
-  void* y = wsb + pl.y_off;
   if (!(s.flags & MOE_F_CHECK_FINITE)) {
     const PermPtrs pp = perm ? perm_ptrs(*perm) : ws_perm(s, pl, workspace);
     hipError_t e = launch_route(s, pl, x, w_router, router_bias, topk_ids, topk_w, nullptr,
                                 workspace, stream);
     if (e == hipSuccess) e = launch_permute(s, pl, topk_ids, pp, tiles, workspace, stream);
-    if (e == hipSuccess) e = launch_ffn(s, pl, x, *experts, pp.sorted_pair, tiles, h, y, stream);
-    if (e == hipSuccess) e = launch_combine(s, y, pp.pair_row, topk_w, residual, out, stream);
+    if (e == hipSuccess) e = ffn_and_combine(s, pl, x, *experts, pp, tiles, topk_w, residual, out, workspace, stream);
     return device_status(e);
   }
   // private results (ids, weights, permutation, output), checked, then published
@@ -490,8 +571,7 @@ int moe_layer(const moe_shape* shape, const void* x, const void* w_router, const
     e = launch_check_finite(wsb + pl.logits_off, static_cast<size_t>(s.T) * s.E, false, kBadLogits,
                             status, stream);
   if (e == hipSuccess) e = launch_permute(s, pl, pids, wp, tiles, workspace, stream);
-  if (e == hipSuccess) e = launch_ffn(s, pl, x, *experts, wp.sorted_pair, tiles, h, y, stream);
-  if (e == hipSuccess) e = launch_combine(s, y, wp.pair_row, pw, residual, pout, stream);
+  if (e == hipSuccess) e = ffn_and_combine(s, pl, x, *experts, wp, tiles, pw, residual, pout, workspace, stream);
   if (e == hipSuccess) e = launch_check_finite(pout, TH, bf, kBadOut, status, stream);
   if ((st = finite_status(pl, workspace, stream, e))) return st;
   e = publish(out, pout, TH * ab, stream);

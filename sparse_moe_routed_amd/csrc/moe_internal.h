@@ -31,6 +31,8 @@ struct Plan {
   size_t w_off;           // float [P]
   size_t out_off;         // act [T][H] (moe_layer)
   size_t status_off;      // uint32 status word
+  // MOE_F_FUSED_FFN: float [I/64][P][H] partial expert outputs
+  size_t part_off;
   size_t total;
 };
 
@@ -59,6 +61,14 @@ hipError_t launch_down(const moe_shape& s, const Plan& pl, const void* h, const 
 hipError_t launch_ffn(const moe_shape& s, const Plan& pl, const void* x, const moe_experts& ex,
                       const int32_t* sorted_pair, const int32_t* tiles, void* h, void* y,
                       hipStream_t st);
+int fused_slices(const moe_shape& s);   // I / 64
+hipError_t launch_ffn_fused(const moe_shape& s, const Plan& pl, const void* x,
+                            const moe_experts& ex, const int32_t* sorted_pair,
+                            const int32_t* tiles, float* part, int wave_tiles, uint64_t* clock,
+                            hipStream_t st);
+hipError_t launch_reduce_parts(const moe_shape& s, const float* part, void* y, hipStream_t st);
+hipError_t launch_combine_parts(const moe_shape& s, const float* part, const int32_t* pair_row,
+                                const float* w, const void* residual, void* out, hipStream_t st);
 hipError_t launch_tile_experts(const moe_shape& s, const moe_experts& src, const moe_experts& dst,
                                hipStream_t st);
 int locality_blocks(int T);   // sum over B = 1..5 of ceil(T / B)

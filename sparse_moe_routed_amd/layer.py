@@ -11,8 +11,9 @@ class MoELayerBuffers:
     """Outputs, permutation arrays and workspace for a shape, on one device."""
 
     def __init__(self, T, H, E, I, top_k, act="bf16", wfmt="dense", device="cuda", tiled=False,
-                 check_finite=False):
-        flags = (_abi.MOE_F_TILED_WEIGHTS if tiled else 0) | (_abi.MOE_F_CHECK_FINITE if check_finite else 0)
+                 check_finite=False, fused=False):
+        flags = ((_abi.MOE_F_TILED_WEIGHTS if tiled else 0) | (_abi.MOE_F_CHECK_FINITE if check_finite else 0)
+                 | (_abi.MOE_F_FUSED_FFN if fused else 0))
         self.shape = _abi.make_shape(T, H, E, I, top_k, act, wfmt, flags)
         self.T, self.H, self.E, self.I, self.k = T, H, E, I, top_k
         self.act = act
@@ -44,6 +45,11 @@ class MoELayerBuffers:
     def permute(self, topk_ids=None, stream=None):
         return _abi.moe_permute(self.shape, self.topk_ids if topk_ids is None else topk_ids,
                                 self.perm, self.workspace, self.ws_bytes, stream)
+
+    def ffn_fused(self, x, experts, wave_tiles=0, item_clock=None, perm=None, stream=None):
+        """moe_ffn_fused into self.y (needs fused=True and tiled=True)."""
+        return _abi.moe_ffn_fused(self.shape, x, experts, self.perm if perm is None else perm, self.y,
+                                  wave_tiles, item_clock, self.workspace, self.ws_bytes, stream)
 
     def stage_experts(self, src, dst, parts=None, stream=None):
         """Copy the records of this call's active experts (the permutation

@@ -103,9 +103,9 @@ def make_case(cfg: MoEConfig, layer: int = 0, x: torch.Tensor | None = None) -> 
     return case
 
 
-def buffers(cfg: MoEConfig, tiled: bool = False) -> M.MoELayerBuffers:
+def buffers(cfg: MoEConfig, tiled: bool = False, fused: bool = False) -> M.MoELayerBuffers:
     return M.MoELayerBuffers(cfg.T, cfg.H, cfg.E, cfg.I, cfg.k, cfg.act, cfg.wfmt, device=DEV,
-                             tiled=tiled)
+                             tiled=tiled, fused=fused)
 
 
 def check_routes(ids_gpu, w_gpu, logits64, ids_ref, w_ref, k):

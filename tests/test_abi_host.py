@@ -247,3 +247,37 @@ def test_stage_experts_validation():
     # pageable host memory is not device-readable: rejected before any launch
     assert M.moe_stage_experts(s, src, dst, pm, stream=0, check=False) == 12
     assert all(v.untouched() for v in b.values())
+
+
+def test_fused_flag_domain_and_workspace():
+    assert M.moe_workspace_size(shape(flags=4)) == 0                # needs the tiled layout
+    base = M.moe_workspace_size(shape(flags=1))
+    fused = M.moe_workspace_size(shape(flags=5))
+    P = 8 * 10
+    assert fused - base >= (640 // 64) * P * 2560 * 4              # float32 partials per slice
+    assert M.moe_workspace_size(shape(flags=5, T=1638)) > 0         # T*k = 16380
+    assert M.moe_workspace_size(shape(flags=5, T=1639)) == 0        # beyond the partial buffer limit
+    assert M.moe_ffn_fused_items(shape(flags=1)) == 0
+    assert M.moe_ffn_fused_items(shape(flags=5)) == (P // 16 + P) * (640 // 64)
+
+
+def test_ffn_fused_validation():
+    b = bufs()
+    s = shape(E=4, top_k=2, H=128, I=128, T=8, flags=5)
+    ex = M.make_experts(b["g"].addr, b["u"].addr, b["d"].addr)
+    pm = M.make_perm(*(b[n].addr for n in ("ids", "w", "logits", "res", "y", "x")))
+    args = dict(x=b["x"].addr, experts=ex, perm=pm, y=b["out"].addr, wave_tiles=0, item_clock=None,
+                workspace=b["ws"].addr, workspace_bytes=1 << 40, stream=0, check=False)
+
+    def call(sh=s, **over):
+        a = dict(args)
+        a.update(over)
+        return M.moe_ffn_fused(sh, **a)
+
+    assert call(sh=shape(E=4, top_k=2, H=128, I=128, T=8, flags=1)) == 10   # flag missing
+    assert call(wave_tiles=-1) == 2
+    assert call(x=None) == 1
+    assert call(item_clock=b["gs"].addr + 8) == 5
+    assert call(item_clock=b["out"].addr) == 6                               # clock over y
+    assert call(workspace_bytes=16) == 7
+    assert all(v.untouched() for v in b.values())

@@ -204,13 +204,18 @@ def _full_layer_check(cfg, layer, n_sample, seed):
     keep, perm = _oracle_perm_tensors(ref.perm)
     rows = ref.perm.pair_row[(sample[:, None] * cfg.k + np.arange(cfg.k)).reshape(-1)]
     res = case.li.x if cfg.residual else None
-    for tiled in (False, True):
-        b2 = buffers(cfg, tiled)
-        say(f"[full {cfg.name} layer {layer} tiled={tiled}] grouped ffn on oracle permutation")
-        b2.grouped_ffn(case.li.x, case.experts(tiled), perm=perm)
+    for tiled, fused in ((False, False), (True, False), (True, True)):
+        if fused and cfg.T * cfg.k > 16384:
+            continue
+        b2 = buffers(cfg, tiled, fused)
+        say(f"[full {cfg.name} layer {layer} tiled={tiled} fused={fused}] ffn on oracle permutation")
+        if fused:
+            b2.ffn_fused(case.li.x, case.experts(tiled), perm=perm)
+        else:
+            b2.grouped_ffn(case.li.x, case.experts(tiled), perm=perm)
         sync()
         yv = check_values(decode(b2.y, cfg.act)[rows], ref.Y[rows], cfg.act, "Y")
-        say(f"[full {cfg.name} layer {layer} tiled={tiled}] Y {yv}; fused layer")
+        say(f"[full {cfg.name} layer {layer} tiled={tiled} fused={fused}] Y {yv}; moe_layer")
         b2.layer(case.li.x, case.li.w_router, case.li.bias, case.experts(tiled), residual=res)
         sync()
         ids = b2.topk_ids.cpu().numpy()
@@ -746,3 +751,66 @@ def test_stage_experts_none_active_and_pageable():
     st = M.moe_stage_experts(b.shape, M.make_experts(*(pageable[n] for n in EXPERT_PIECES)), dst,
                              b.perm, check=False)
     assert st == 12
+
+
+# --------------------------------------------------------------------------
+# Fused gate/up -> down component waves (moe_ffn_fused, MOE_F_FUSED_FFN)
+# --------------------------------------------------------------------------
+
+FUSED_CASES = [n for n in SMALL if tiled_ok(SMALL[n]) and SMALL[n].T * SMALL[n].k <= 16384]
+
+
+@pytest.mark.parametrize("name", FUSED_CASES)
+@pytest.mark.parametrize("wave", [0, 1, 2, 4])
+def test_ffn_fused(name, wave):
+    """moe_ffn_fused on the oracle permutation against the oracle's expert
+    outputs, for waves of 1, 2, 4 and all tiles."""
+    case, ref = get(name)
+    cfg = case.cfg
+    buf = buffers(cfg, tiled=True, fused=True)
+    keep, perm = _oracle_perm_tensors(ref.perm)
+    say(f"[fused {name} wave={wave}] moe_ffn_fused on oracle permutation")
+    buf.ffn_fused(case.li.x, case.experts(True), wave_tiles=wave, perm=perm)
+    sync()
+    stats = check_values(decode(buf.y, cfg.act), ref.Y, cfg.act, "Y")
+    say(f"[fused {name} wave={wave}] Y {stats}")
+
+
+@pytest.mark.parametrize("name", FUSED_CASES)
+def test_layer_fused(name):
+    """moe_layer with MOE_F_FUSED_FFN (fused FFN + combine of the partial
+    results) against the oracle layer."""
+    case, ref = get(name)
+    cfg = case.cfg
+    buf = buffers(cfg, tiled=True, fused=True)
+    res = case.li.x if cfg.residual else None
+    say(f"[fused {name}] moe_layer")
+    buf.layer(case.li.x, case.li.w_router, case.li.bias, case.experts(True), residual=res)
+    sync()
+    stats, same = check_routes(buf.topk_ids.cpu().numpy(), buf.topk_w.cpu().numpy().astype(np.float64),
+                               ref.logits, ref.ids, ref.w, cfg.k)
+    vs = check_values(decode(buf.out, cfg.act)[same], ref.out[same], cfg.act, "out")
+    say(f"[fused {name}] layer routes {stats} out {vs}")
+
+
+@pytest.mark.parametrize("wave", [0, 2])
+def test_fused_item_clock(wave):
+    """Item clock of moe_ffn_fused: for every item of the plan start <=
+    gate/up done <= down done; entries past the last item stay untouched."""
+    case, ref = get("int4_small")
+    cfg = case.cfg
+    buf = buffers(cfg, tiled=True, fused=True)
+    keep, perm = _oracle_perm_tensors(ref.perm)
+    cap = M.moe_ffn_fused_items(buf.shape)
+    clock = torch.full((3 * cap,), -1, dtype=torch.int64, device=DEV)
+    buf.ffn_fused(case.li.x, case.experts(True), wave_tiles=wave, item_clock=clock, perm=perm)
+    sync()
+    rt = 16 * (1 if cfg.T <= 16 or cfg.T * cfg.k <= 12 * cfg.E else (2 if cfg.T <= 1024 else 4))
+    counts = ref.perm.counts
+    n_tiles = int(sum((c + rt - 1) // rt for c in counts if c > 0))
+    n_items = n_tiles * (cfg.I // 64)
+    c = clock.view(-1, 3).cpu().numpy()
+    assert (c[:n_items] > 0).all()
+    assert (c[:n_items, 0] <= c[:n_items, 1]).all() and (c[:n_items, 1] <= c[:n_items, 2]).all()
+    assert (c[n_items:] == -1).all()
+    assert M.moe_device_clock_khz() > 0

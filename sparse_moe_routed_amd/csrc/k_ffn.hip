@@ -367,14 +367,14 @@ __global__ __launch_bounds__(256) void k_gateup_t(
     if constexpr (WF != WF_BF16) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        S.sc[mb][0] = tscales(Sg, mb, u, r);
-        S.sc[mb][1] = tscales(Su, mb, u, r);
+        S.sc[mb][0] = tscales<WF, weight_aux<NB>()>(Sg, mb, u, r);
+        S.sc[mb][1] = tscales<WF, weight_aux<NB>()>(Su, mb, u, r);
       }
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      S.raw[mb][0] = tload<WF>(Sg, mb, u, lane);
-      S.raw[mb][1] = tload<WF>(Su, mb, u, lane);
+      S.raw[mb][0] = tload<WF, weight_aux<NB>()>(Sg, mb, u, lane);
+      S.raw[mb][1] = tload<WF, weight_aux<NB>()>(Su, mb, u, lane);
     }
 #pragma unroll
     for (int st = 0; st < 4; ++st)
@@ -502,10 +502,10 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
   auto load = [&](Stage& S, int u) {
     if constexpr (WF != WF_BF16) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) S.sc[mb] = tscales(Sd, mb, u, r);
+      for (int mb = 0; mb < MB; ++mb) S.sc[mb] = tscales<WF, weight_aux<NB>()>(Sd, mb, u, r);
     }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) S.raw[mb] = tload<WF>(Sd, mb, u, lane);
+    for (int mb = 0; mb < MB; ++mb) S.raw[mb] = tload<WF, weight_aux<NB>()>(Sd, mb, u, lane);
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
@@ -615,14 +615,14 @@ __global__ __launch_bounds__(256) void k_gateup_x(
     if constexpr (WF != WF_BF16) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        sc[mb][0] = tscales(Sg, mb, u, r);
-        sc[mb][1] = tscales(Su, mb, u, r);
+        sc[mb][0] = tscales<WF, weight_aux<NB>()>(Sg, mb, u, r);
+        sc[mb][1] = tscales<WF, weight_aux<NB>()>(Su, mb, u, r);
       }
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      raw[mb][0] = tload<WF>(Sg, mb, u, lane);
-      raw[mb][1] = tload<WF>(Su, mb, u, lane);
+      raw[mb][0] = tload<WF, weight_aux<NB>()>(Sg, mb, u, lane);
+      raw[mb][1] = tload<WF, weight_aux<NB>()>(Su, mb, u, lane);
     }
     if (u + 1 < units) xu.load(u + 1);
     SCHED_FENCE();
@@ -716,10 +716,10 @@ __global__ __launch_bounds__(256) void k_down_x(const uint16_t* __restrict__ h,
     TRaw<WF> raw[MB];
     if constexpr (WF != WF_BF16) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) sc[mb] = tscales(Sd, mb, u, r);
+      for (int mb = 0; mb < MB; ++mb) sc[mb] = tscales<WF, weight_aux<NB>()>(Sd, mb, u, r);
     }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) raw[mb] = tload<WF>(Sd, mb, u, lane);
+    for (int mb = 0; mb < MB; ++mb) raw[mb] = tload<WF, weight_aux<NB>()>(Sd, mb, u, lane);
     if (u + 1 < units) xu.load(u + 1);
     SCHED_FENCE();
     const char* buf = xs[u & 1];

@@ -88,11 +88,11 @@ __global__ __launch_bounds__(256) void k_ffn_fused(
     for (int v = 0; v < US; ++v) {
       const int u = min(u0 + v, units - 1);   // a tail batch reloads the last unit, unused
       if constexpr (WF != WF_BF16) {
-        sc[v][0] = tscales(Sg, 0, u, r);
-        sc[v][1] = tscales(Su, 0, u, r);
+        sc[v][0] = tscales<WF, weight_aux<NB>()>(Sg, 0, u, r);
+        sc[v][1] = tscales<WF, weight_aux<NB>()>(Su, 0, u, r);
       }
-      raw[v][0] = tload<WF>(Sg, 0, u, lane);
-      raw[v][1] = tload<WF>(Su, 0, u, lane);
+      raw[v][0] = tload<WF, weight_aux<NB>()>(Sg, 0, u, lane);
+      raw[v][1] = tload<WF, weight_aux<NB>()>(Su, 0, u, lane);
 #pragma unroll
       for (int st = 0; st < 4; ++st)
 #pragma unroll
@@ -172,16 +172,17 @@ __global__ __launch_bounds__(256) void k_ffn_fused(
 #pragma unroll
         for (int c = 0; c < 2; ++c)
           wb[i][c] = __builtin_amdgcn_raw_buffer_load_b128(Sd.w, lane * 16,
-                                                           (m * (I / 32) + 2 * sl + c) * 1024, 0);
+                                                           (m * (I / 32) + 2 * sl + c) * 1024, weight_aux<NB>());
       } else if constexpr (WF == WF_INT4) {
         w4[i] = __builtin_amdgcn_raw_buffer_load_b64(Sd.w, lane * 16 + 8 * hf,
-                                                     (m * (I / 128) + kb) * 1024, 0);
+                                                     (m * (I / 128) + kb) * 1024, weight_aux<NB>());
       } else {
         w2[i] = __builtin_amdgcn_raw_buffer_load_b32(Sd.w, lane * 8 + 4 * hf,
-                                                     (m * (I / 128) + kb) * 512, 0);
+                                                     (m * (I / 128) + kb) * 512, weight_aux<NB>());
       }
       if constexpr (WF != WF_BF16)
-        scd[i] = __builtin_amdgcn_raw_buffer_load_b32(Sd.s, r * 8 + 4 * hf, (m * (I / 128) + kb) * 128, 0);
+        scd[i] = __builtin_amdgcn_raw_buffer_load_b32(Sd.s, r * 8 + 4 * hf, (m * (I / 128) + kb) * 128,
+                                                      weight_aux<NB>());
     }
     SCHED_FENCE();
 #pragma unroll

@@ -1,6 +1,5 @@
 // Device code shared by the routing kernels: router logits of small batches
-// and the exact top-k of one token (used by the top-k kernel and by the
-// small-batch top-k + permutation kernel).
+// and the exact top-k of one token (used by the top-k kernel).
 //
 // Reference: "Agent Field Notes -- full corpus", AFN-001, section "Phase 1:
 // separate math from acceleration" (float32 router softmax and normalized
@@ -37,7 +36,7 @@ __device__ __forceinline__ void router_part(const uint16_t* __restrict__ x,
 #pragma unroll
     for (int u = 0; u < kRouterBatch; ++u) {
       if (c + u < cpp) {
-        a[u] = ld16(wp + (c + u) * 32);
+        a[u] = ld16_stream(wp + (c + u) * 32);
         b[u] = ld16(xp + (c + u) * 32);
       }
     }

@@ -30,6 +30,38 @@ struct Tile {
 // one unit pays the memory latency several times over.
 #define SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
+// The k loop over units u0 .. u1-1 of one wave: load(stage, u) issues a
+// unit's loads, compute(stage) consumes them.  With PF the loads of unit
+// u+1 are issued before unit u is multiplied (two register stages), so a
+// wave always has one unit in flight; without it, load and compute
+// alternate and the other waves of the SIMD hide the latency.
+template <bool PF, typename Stage, typename Load, typename Compute>
+__device__ __forceinline__ void unit_loop(int u0, int u1, Load&& load, Compute&& compute) {
+  if constexpr (!PF) {
+    for (int u = u0; u < u1; ++u) {
+      Stage s;
+      load(s, u);
+      SCHED_FENCE();
+      compute(s);
+    }
+  } else {
+    Stage a, b;
+    load(a, u0);
+    int u = u0;
+    for (; u + 1 < u1; u += 2) {
+      load(b, u + 1);
+      SCHED_FENCE();
+      compute(a);
+      SCHED_FENCE();
+      if (u + 2 < u1) load(a, u + 2);
+      SCHED_FENCE();
+      compute(b);
+      SCHED_FENCE();
+    }
+    if (u < u1) compute(a);
+  }
+}
+
 __device__ __forceinline__ Tile read_tile(const int32_t* tiles, int t) {
   return Tile{tiles[3 * t], tiles[3 * t + 1], tiles[3 * t + 2]};
 }

@@ -17,27 +17,29 @@ namespace moe {
 
 // bf16 router.  The dot product over H is cut into `nparts` parts of
 // `cpp` chunks of 32 (nparts = the largest divisor of H/32 that is <= 16, so
-// the cut depends on H alone).  Each v_mfma_f32_16x16x32_bf16 sums the 32
-// exact bf16 products of a chunk in float32; the chunk sums of a part are
-// added in float64 in k order, the part sums are added in part order, the
-// bias is added, and the total is rounded once to float32.  Both kernels
-// below use exactly this association, so a token's logits are bit-identical
-// whatever the batch size or the kernel that computed them.
+// the cut depends on H alone), and the parts into groups of kRouterGroup
+// consecutive parts (the last group may be shorter).  Each
+// v_mfma_f32_16x16x32_bf16 sums the 32 exact bf16 products of a chunk in
+// float32; the chunk sums of a part are added in float64 in k order, the
+// part sums of a group in part order, the group sums in group order, then
+// the bias is added and the total is rounded once to float32.  Every path
+// below uses exactly this association, so a token's logits are
+// bit-identical whatever the batch size or the kernels that computed them.
 
-// Small batches: one 16-token x 16-expert tile per workgroup, one wave per
-// part, part sums combined through LDS.  grid (ceil(T/16), ceil(E/16)),
-// block 64 * nparts.
-__global__ __launch_bounds__(1024) void k_router_parts(const uint16_t* __restrict__ x,
-                                                       const uint16_t* __restrict__ wr,
-                                                       const float* __restrict__ bias, int T,
-                                                       int H, int E, int nparts,
-                                                       float* __restrict__ logits) {
-  __shared__ double red[16][64][4];
+// Small batches: one workgroup per (16-token x 16-expert tile, group of
+// parts), one wave per part; the group's part sums are added through LDS and
+// stored in float64 to gsum[group][T][E] (the top-k kernel finishes the
+// logits).  grid (ceil(T/16), ceil(E/16), ngroups), block 64 * kRouterGroup.
+__global__ __launch_bounds__(64 * kRouterGroup) void k_router_parts(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int H, int E,
+    int nparts, double* __restrict__ gsum) {
+  __shared__ double red[kRouterGroup][64][4];
   const int wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
-  router_part(x, wr, T, H, E, nparts, t0, e0, wave, red);
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16, g = blockIdx.z;
+  const int p0 = g * kRouterGroup, np = min(kRouterGroup, nparts - p0);
+  if (wave < np) router_part(x, wr, T, H, E, nparts, t0, e0, p0 + wave, red[wave]);
   __syncthreads();
-  if (wave == 0) router_store(red, bias, T, E, nparts, t0, e0, logits);
+  if (wave == 0) router_group_store(red, np, T, E, t0, e0, gsum + static_cast<size_t>(g) * T * E);
 }
 
 // Larger batches: workgroup tile of 32 A tokens x 32 A experts, four waves
@@ -67,13 +69,13 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t* __restrict__
   xu.init(x, [&](int R) { return static_cast<size_t>(min(tb + R, T - 1)) * H; });
   wu.init(wr, [&](int R) { return static_cast<size_t>(min(eb + R, E - 1)) * H; });
 
-  double part[A][A][4], tot[A][A][4];
+  double part[A][A][4], grp[A][A][4], tot[A][A][4];
 #pragma unroll
   for (int a = 0; a < A; ++a)
 #pragma unroll
     for (int i = 0; i < A; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) part[a][i][j] = tot[a][i][j] = 0.0;
+      for (int j = 0; j < 4; ++j) part[a][i][j] = grp[a][i][j] = tot[a][i][j] = 0.0;
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 
   xu.load(0);
@@ -103,15 +105,21 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t* __restrict__
 #pragma unroll
           for (int j = 0; j < 4; ++j) part[a][i][j] += static_cast<double>(f[j]);
         }
-      if ((4 * u + st + 1) % cpp == 0) {
+      if ((4 * u + st + 1) % cpp == 0) {            // a part ends
+        const int p = (4 * u + st) / cpp;
+        const bool gend = (p + 1) % kRouterGroup == 0 || p + 1 == nparts;
 #pragma unroll
         for (int a = 0; a < A; ++a)
 #pragma unroll
           for (int i = 0; i < A; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              tot[a][i][j] += part[a][i][j];
+              grp[a][i][j] += part[a][i][j];
               part[a][i][j] = 0.0;
+              if (gend) {
+                tot[a][i][j] += grp[a][i][j];
+                grp[a][i][j] = 0.0;
+              }
             }
       }
     }
@@ -143,10 +151,14 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t* __restrict__
 int router_parts(int H) {
   const int chunks = H / 32;
   int best = 1;
-  for (int d = 1; d <= 16; ++d)
+  for (int d = 1; d <= kRouterMaxParts; ++d)
     if (chunks % d == 0) best = d;
   return best;
 }
+
+int router_groups(int H) { return (router_parts(H) + kRouterGroup - 1) / kRouterGroup; }
+
+bool router_small(const moe_shape& s) { return s.act == MOE_DT_BF16 && s.T <= 64; }
 
 // float32 router: one thread per (token, expert), products and sums in
 // float64 in ascending h, bias added, rounded once to float32.
@@ -165,31 +177,94 @@ __global__ __launch_bounds__(256) void k_router_f32(const float* __restrict__ x,
   logits[idx] = static_cast<float>(s);
 }
 
-// Exact top-k, one wave per token (topk_token).  grid ceil(T/4), block 256.
+// Exact top-k of logits already finished (f32 router, LDS router): one wave
+// per token (topk_select).  grid ceil(T/4), block 256.
 template <int NV>
 __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, int T, int E, int k,
                                               int32_t* __restrict__ ids, float* __restrict__ w) {
   __shared__ float sel[4][1024];
-  const int wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;   // whole wave leaves; no workgroup barrier below
+  const float* lt = logits + static_cast<size_t>(t) * E;
+  float v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = lt[min(j * 64 + lane, E - 1)];
   const size_t o = static_cast<size_t>(t) * k;
-  topk_token<NV>(logits + static_cast<size_t>(t) * E, E, k, sel[wave], ids + o, w + o, nullptr);
+  topk_select<NV>(v, E, k, sel[wave], ids + o, w + o);
+}
+
+// Small bf16 batches: finish the logits of one token from the router's
+// group sums, then its exact top-k.  Workgroup per token; wave w finishes
+// the experts of slots w, w+4, ... (the ngroups float64 group sums, all
+// loaded before any is added, summed in group order, bias added, rounded
+// once to float32) into LDS and `logits`; after a barrier wave 0 selects.
+// grid T, block 256.
+template <int NV>
+__global__ __launch_bounds__(256) void k_topk_groups(const double* __restrict__ gsum, int ngroups,
+                                                     const float* __restrict__ bias,
+                                                     float* __restrict__ logits, int T, int E, int k,
+                                                     int32_t* __restrict__ ids,
+                                                     float* __restrict__ w) {
+  constexpr int NJ = (NV + 3) / 4;   // slots per wave
+  __shared__ float lv[NV * 64];
+  __shared__ float sel[1024];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x;
+  const size_t slice = static_cast<size_t>(T) * E;
+  const double* gt = gsum + static_cast<size_t>(t) * E;
+  double gv[kRouterMaxGroups][NJ];
+  float bv[NJ];
+#pragma unroll
+  for (int i = 0; i < NJ; ++i) {
+    const int e = min((wave + 4 * i) * 64 + lane, E - 1);
+#pragma unroll
+    for (int g = 0; g < kRouterMaxGroups; ++g) gv[g][i] = g < ngroups ? gt[g * slice + e] : 0.0;
+    bv[i] = bias ? bias[e] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < NJ; ++i) {
+    const int j = wave + 4 * i;
+    if (j >= NV) break;
+    double sv = gv[0][i];
+#pragma unroll
+    for (int g = 1; g < kRouterMaxGroups; ++g)
+      if (g < ngroups) sv += gv[g][i];
+    if (bias) sv += static_cast<double>(bv[i]);
+    const float f = static_cast<float>(sv);
+    lv[j * 64 + lane] = f;
+    if (j * 64 + lane < E) logits[static_cast<size_t>(t) * E + j * 64 + lane] = f;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  float v[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) v[j] = lv[j * 64 + lane];
+  const size_t o = static_cast<size_t>(t) * k;
+  topk_select<NV>(v, E, k, sel, ids + o, w + o);
 }
 
 template <int NV>
-static void launch_topk(const moe_shape& s, const float* lg, int32_t* ids, float* w, hipStream_t st) {
-  hipLaunchKernelGGL((k_topk<NV>), dim3((s.T + 3) / 4), dim3(256), 0, st, lg, s.T, s.E, s.top_k, ids, w);
+static void launch_topk(const moe_shape& s, const double* gsum, int ngroups, const float* bias,
+                        float* lg, int32_t* ids, float* w, hipStream_t st) {
+  if (gsum)
+    hipLaunchKernelGGL((k_topk_groups<NV>), dim3(s.T), dim3(256), 0, st, gsum, ngroups, bias, lg,
+                       s.T, s.E, s.top_k, ids, w);
+  else
+    hipLaunchKernelGGL((k_topk<NV>), dim3((s.T + 3) / 4), dim3(256), 0, st, lg, s.T, s.E, s.top_k,
+                       ids, w);
 }
 
+// The router logits, or (small bf16 batches) their group sums in `gsum`.
 static hipError_t launch_router(const moe_shape& s, const void* x, const void* w_router,
-                                const float* bias, float* lg, hipStream_t st) {
+                                const float* bias, float* lg, double* gsum, hipStream_t st) {
   if (s.act == MOE_DT_BF16) {
     const int np = router_parts(s.H);
-    if (s.T <= 64) {
-      dim3 grid((s.T + 15) / 16, (s.E + 15) / 16);
-      hipLaunchKernelGGL(k_router_parts, grid, dim3(64 * np), 0, st, static_cast<const uint16_t*>(x),
-                         static_cast<const uint16_t*>(w_router), bias, s.T, s.H, s.E, np, lg);
+    if (gsum) {
+      dim3 grid((s.T + 15) / 16, (s.E + 15) / 16, router_groups(s.H));
+      hipLaunchKernelGGL(k_router_parts, grid, dim3(64 * kRouterGroup), 0, st,
+                         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
+                         s.T, s.H, s.E, np, gsum);
     } else if (s.T <= 1024) {
       dim3 grid((s.T + 31) / 32, (s.E + 31) / 32);
       hipLaunchKernelGGL(k_router_lds<1>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x),
@@ -212,14 +287,17 @@ hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const
                         const float* bias, int32_t* ids, float* w, float* logits, void* ws,
                         hipStream_t st) {
   float* lg = logits ? logits : reinterpret_cast<float*>(static_cast<char*>(ws) + pl.logits_off);
-  hipError_t e = launch_router(s, x, w_router, bias, lg, st);
+  double* gsum = router_small(s) ? reinterpret_cast<double*>(static_cast<char*>(ws) + pl.gsum_off)
+                                 : nullptr;
+  hipError_t e = launch_router(s, x, w_router, bias, lg, gsum, st);
   if (e != hipSuccess) return e;
-  const int nv = (s.E + 63) / 64;
-  if (nv <= 1) launch_topk<1>(s, lg, ids, w, st);
-  else if (nv <= 2) launch_topk<2>(s, lg, ids, w, st);
-  else if (nv <= 4) launch_topk<4>(s, lg, ids, w, st);
-  else if (nv <= 8) launch_topk<8>(s, lg, ids, w, st);
-  else launch_topk<16>(s, lg, ids, w, st);
+  const int nv = (s.E + 63) / 64, ng = router_groups(s.H);
+  const float* fb = gsum ? bias : nullptr;   // the other paths added the bias already
+  if (nv <= 1) launch_topk<1>(s, gsum, ng, fb, lg, ids, w, st);
+  else if (nv <= 2) launch_topk<2>(s, gsum, ng, fb, lg, ids, w, st);
+  else if (nv <= 4) launch_topk<4>(s, gsum, ng, fb, lg, ids, w, st);
+  else if (nv <= 8) launch_topk<8>(s, gsum, ng, fb, lg, ids, w, st);
+  else launch_topk<16>(s, gsum, ng, fb, lg, ids, w, st);
   return hipGetLastError();
 }
 

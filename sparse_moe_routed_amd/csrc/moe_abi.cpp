@@ -54,6 +54,10 @@ bool make_plan(const moe_shape& s, Plan* p) {
   size_t off = 0;
   p->logits_off = off;
   off = align_up(off + static_cast<size_t>(T) * s.E * sizeof(float), 256);
+  if (router_small(s)) {
+    p->gsum_off = off;
+    off = align_up(off + static_cast<size_t>(router_groups(s.H)) * T * s.E * sizeof(double), 256);
+  }
   p->chunk_off = off;
   off = align_up(off + static_cast<size_t>(p->chunks) * s.E * 2 * sizeof(int32_t), 256);
   p->perm_off = off;

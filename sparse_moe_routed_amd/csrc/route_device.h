@@ -1,5 +1,5 @@
-// Device code shared by the routing kernels: router logits of small batches
-// and the exact top-k of one token (used by the top-k kernel).
+// Device code of the routing kernels: the part sums of small-batch router
+// logits and the exact top-k of one token.
 //
 // Reference: "Agent Field Notes -- full corpus", AFN-001, section "Phase 1:
 // separate math from acceleration" (float32 router softmax and normalized
@@ -12,15 +12,17 @@
 namespace moe {
 
 constexpr int kRouterBatch = 8;
+constexpr int kRouterGroup = 4;       // consecutive H parts whose sums are added first
+constexpr int kRouterMaxParts = 16;
+constexpr int kRouterMaxGroups = kRouterMaxParts / kRouterGroup;
 
-// One part of a 16-token x 16-expert logit tile (wave `part` of the
-// workgroup): float32 chunk sums from MFMA, added in float64 in k order.
-// red[part][lane][j] receives the part sum of expert e0 + 4q + j, token
-// t0 + r (lane = r + 16 q).
+// One part of a 16-token x 16-expert logit tile, by one wave: float32
+// chunk sums from MFMA, added in float64 in k order.  slot[lane][j]
+// receives the part sum of expert e0 + 4q + j, token t0 + r (lane = r + 16 q).
 __device__ __forceinline__ void router_part(const uint16_t* __restrict__ x,
                                             const uint16_t* __restrict__ wr, int T, int H, int E,
                                             int nparts, int t0, int e0, int part,
-                                            double (*red)[64][4]) {
+                                            double (*slot)[4]) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
   const int cpp = H / 32 / nparts;
@@ -50,15 +52,14 @@ __device__ __forceinline__ void router_part(const uint16_t* __restrict__ x,
     }
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) red[part][lane][j] = acc[j];
+  for (int j = 0; j < 4; ++j) slot[lane][j] = acc[j];
 }
 
-// Wave 0 after a barrier: part sums added in part order, bias added,
-// rounded once to float32 and stored.
-__device__ __forceinline__ void router_store(const double (*red)[64][4],
-                                             const float* __restrict__ bias, int T, int E,
-                                             int nparts, int t0, int e0,
-                                             float* __restrict__ logits) {
+// Wave 0 after a barrier: the `np` part sums of one group added in part
+// order (float64) and stored to gsum[t][e] (the group's slice [T][E]).
+__device__ __forceinline__ void router_group_store(const double (*red)[64][4], int np, int T,
+                                                   int E, int t0, int e0,
+                                                   double* __restrict__ gsum) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
   const int t = t0 + r;
@@ -68,30 +69,25 @@ __device__ __forceinline__ void router_store(const double (*red)[64][4],
     const int e = e0 + 4 * q + j;
     if (e < E) {
       double s = red[0][lane][j];
-      for (int w = 1; w < nparts; ++w) s += red[w][lane][j];
-      if (bias) s += static_cast<double>(bias[e]);
-      logits[static_cast<size_t>(t) * E + e] = static_cast<float>(s);
+      for (int w = 1; w < np; ++w) s += red[w][lane][j];
+      gsum[static_cast<size_t>(t) * E + e] = s;
     }
   }
 }
 
-// Exact top-k of one token by one wave; lane l holds the logits of experts
-// l, 64 + l, ... (NV slots, E <= 64 NV).  Each of the k rounds takes the
-// wave maximum m of the remaining logits, then the smallest expert index
-// whose logit equals m -- the total order (logit descending, index
-// ascending) -- with DPP row reductions and readlanes (no LDS round trips).
-// -0.0 and +0.0 compare equal.  Weights: exp(l_j - l_0) / sum over the
-// selected, in float32 (the full softmax renormalized over the selection).
-// `sel` is this wave's LDS scratch of k floats; `ids_lds`, when not null,
-// receives a copy of the ids.
+// Exact top-k of one token by one wave; lane l holds the logits v[j] of
+// experts j*64 + l (NV slots, E <= 64 NV; slots at or past E are ignored).
+// Each of the k rounds takes the wave maximum m of the remaining logits,
+// then the smallest expert index whose logit equals m -- the total order
+// (logit descending, index ascending) -- with DPP row reductions and
+// readlanes (no LDS round trips).  -0.0 and +0.0 compare equal.  Weights:
+// exp(l_j - l_0) / sum over the selected, in float32 (the full softmax
+// renormalized over the selection).  `sel` is this wave's LDS scratch of k
+// floats.
 template <int NV>
-__device__ __forceinline__ void topk_token(const float* __restrict__ lt, int E, int k,
-                                           float* sel, int32_t* __restrict__ ids,
-                                           float* __restrict__ w, int32_t* ids_lds) {
+__device__ __forceinline__ void topk_select(const float (&v)[NV], int E, int k, float* sel,
+                                            int32_t* __restrict__ ids, float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
-  float v[NV];
-#pragma unroll
-  for (int j = 0; j < NV; ++j) v[j] = lt[min(j * 64 + lane, E - 1)];
   uint32_t live = 0;
 #pragma unroll
   for (int j = 0; j < NV; ++j)
@@ -110,7 +106,6 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ lt, int E, 
     if (static_cast<int>(e & 63u) == lane) live &= ~(1u << (e >> 6));
     if (lane == 0) {
       ids[rnk] = static_cast<int32_t>(e);
-      if (ids_lds) ids_lds[rnk] = static_cast<int32_t>(e);
       sel[rnk] = m;
     }
   }

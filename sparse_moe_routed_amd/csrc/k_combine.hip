@@ -14,6 +14,10 @@
 
 namespace moe {
 
+// KB route slots per batch: all index/weight loads of a batch, then all its
+// row loads, then the float32 accumulation in ascending j; KB >= k makes the
+// whole combine two dependent memory round trips.
+template <int KB>
 __global__ __launch_bounds__(256) void k_combine_bf16(const uint16_t* __restrict__ y,
                                                       const int32_t* __restrict__ pair_row,
                                                       const float* __restrict__ w,
@@ -30,22 +34,21 @@ __global__ __launch_bounds__(256) void k_combine_bf16(const uint16_t* __restrict
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   const int32_t* pr = pair_row + static_cast<size_t>(t) * k;
   const float* wt = w + static_cast<size_t>(t) * k;
-  // slots in batches of 8: all index/weight loads, then all row loads, then
-  // the float32 accumulation in ascending j
-  for (int j0 = 0; j0 < k; j0 += 8) {
-    int row[8];
-    float wj[8];
+  const u32x4_t rv = res ? ld16(res + static_cast<size_t>(t) * H + c * 8) : u32x4_t{0u, 0u, 0u, 0u};
+  for (int j0 = 0; j0 < k; j0 += KB) {
+    int row[KB];
+    float wj[KB];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < KB; ++u) {
       const int j = min(j0 + u, k - 1);
       row[u] = min(max(pr[j], 0), P - 1);
       wj[u] = wt[j];
     }
-    u32x4_t v[8];
+    u32x4_t v[KB];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = ld16(y + static_cast<size_t>(row[u]) * H + c * 8);
+    for (int u = 0; u < KB; ++u) v[u] = ld16(y + static_cast<size_t>(row[u]) * H + c * 8);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < KB; ++u) {
       if (j0 + u < k) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -56,7 +59,7 @@ __global__ __launch_bounds__(256) void k_combine_bf16(const uint16_t* __restrict
     }
   }
   if (res) {
-    const u32x4_t v = ld16(res + static_cast<size_t>(t) * H + c * 8);
+    const u32x4_t v = rv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[2 * i] += __uint_as_float(v[i] << 16);
@@ -106,7 +109,8 @@ hipError_t launch_combine(const moe_shape& s, const void* y, const int32_t* pair
                           const float* w, const void* residual, void* out, hipStream_t st) {
   if (s.act == MOE_DT_BF16) {
     const size_t n = static_cast<size_t>(s.T) * (s.H / 8);
-    hipLaunchKernelGGL(k_combine_bf16, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
+    auto kern = s.top_k <= 16 ? k_combine_bf16<16> : k_combine_bf16<8>;
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0,
                        st, static_cast<const uint16_t*>(y), pair_row, w,
                        static_cast<const uint16_t*>(residual), static_cast<uint16_t*>(out), s.T,
                        s.H, s.top_k);

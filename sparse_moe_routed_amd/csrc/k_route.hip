@@ -45,16 +45,22 @@ __global__ __launch_bounds__(64 * kRouterGroup) void k_router_parts(
 // Larger batches: workgroup tile of 32 A tokens x 32 A experts, four waves
 // in 2 x 2, each (16 A) x (16 A).  Token rows and router rows are staged in
 // LDS once per workgroup and 128-wide k unit (in MFMA fragment order), and
-// each wave walks the 32-wide chunks in k order, keeping a float64 part sum
-// and a float64 total per output (the association above).  Two LDS buffers:
-// the next unit is loaded while the current one is multiplied.
-// grid (ceil(T / 32 A), ceil(E / 32 A)), block 256.
-template <int A>
+// each wave walks the 32-wide chunks in k order, keeping float64 part,
+// group and total sums per output (the association above).  Two LDS
+// buffers: the next unit is loaded while the current one is multiplied.
+// GS: one workgroup per (tile, group of parts) covering only that group's
+// units, storing the float64 group sums to gsum[group][T][E] (the top-k
+// kernel finishes the logits); otherwise the whole H and the finished
+// logits.  A group spans whole 128-k units: H/32 = nparts * cpp is a
+// multiple of 4, and so is every group's chunk count.
+// grid (ceil(T / 32 A), ceil(E / 32 A), GS ? groups : 1), block 256.
+template <int A, bool GS>
 __global__ __launch_bounds__(256) void k_router_lds(const uint16_t* __restrict__ x,
                                                     const uint16_t* __restrict__ wr,
                                                     const float* __restrict__ bias, int T, int H,
                                                     int E, int nparts,
-                                                    float* __restrict__ logits) {
+                                                    float* __restrict__ logits,
+                                                    double* __restrict__ gsum) {
   constexpr int NB = 2 * A;   // 16-row blocks per staged tile
   __shared__ __align__(16) char xs[2][NB * 4096];
   __shared__ __align__(16) char wsm[2][NB * 4096];
@@ -63,7 +69,9 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t* __restrict__
   const int tb = blockIdx.x * 32 * A, eb = blockIdx.y * 32 * A;
   const int tblk = (wave & 1) * A, eblk = (wave >> 1) * A;
   const int cpp = H / 32 / nparts;
-  const int units = H / 128;
+  const int g = GS ? static_cast<int>(blockIdx.z) : 0;
+  const int ubeg = GS ? g * cpp : 0;                                   // 4 cpp chunks per group
+  const int units = GS ? min(kRouterGroup * (g + 1), nparts) * cpp / 4 - ubeg : H / 128;
 
   XUnit<NB> xu, wu;
   xu.init(x, [&](int R) { return static_cast<size_t>(min(tb + R, T - 1)) * H; });
@@ -78,15 +86,15 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t* __restrict__
       for (int j = 0; j < 4; ++j) part[a][i][j] = grp[a][i][j] = tot[a][i][j] = 0.0;
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
 
-  xu.load(0);
-  wu.load(0);
+  xu.load(ubeg);
+  wu.load(ubeg);
   xu.store(xs[0]);
   wu.store(wsm[0]);
   __syncthreads();
   for (int u = 0; u < units; ++u) {
     if (u + 1 < units) {
-      xu.load(u + 1);
-      wu.load(u + 1);
+      xu.load(ubeg + u + 1);
+      wu.load(ubeg + u + 1);
     }
     const char* bx = xs[u & 1];
     const char* bw = wsm[u & 1];
@@ -105,8 +113,9 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t* __restrict__
 #pragma unroll
           for (int j = 0; j < 4; ++j) part[a][i][j] += static_cast<double>(f[j]);
         }
-      if ((4 * u + st + 1) % cpp == 0) {            // a part ends
-        const int p = (4 * u + st) / cpp;
+      const int c = 4 * (ubeg + u) + st;            // chunk index in H
+      if ((c + 1) % cpp == 0) {                       // a part ends
+        const int p = c / cpp;
         const bool gend = (p + 1) % kRouterGroup == 0 || p + 1 == nparts;
 #pragma unroll
         for (int a = 0; a < A; ++a)
@@ -139,7 +148,10 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t* __restrict__
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int e = eb + 16 * (eblk + a) + 4 * q + j;
-        if (e < E) {
+        if (e >= E) continue;
+        if constexpr (GS) {
+          gsum[(static_cast<size_t>(g) * T + t) * E + e] = tot[a][i][j];
+        } else {
           double sum = tot[a][i][j];
           if (bias) sum += static_cast<double>(bias[e]);
           logits[static_cast<size_t>(t) * E + e] = static_cast<float>(sum);
@@ -158,7 +170,14 @@ int router_parts(int H) {
 
 int router_groups(int H) { return (router_parts(H) + kRouterGroup - 1) / kRouterGroup; }
 
-bool router_small(const moe_shape& s) { return s.act == MOE_DT_BF16 && s.T <= 64; }
+// Token limit of the group-sum path: one workgroup per group of parts
+// multiplies the parallelism of the router by the group count (512 tokens:
+// 3.7 us less per layer); at 4096 tokens the float64 group sums (groups *
+// T * E * 8 bytes = 64 MB) cost more than the parallelism saves (+13 us),
+// so larger batches let the LDS kernel finish the sums.
+constexpr int kRouterGsumMaxT = 1024;
+
+bool router_gsum(const moe_shape& s) { return s.act == MOE_DT_BF16 && s.T <= kRouterGsumMaxT; }
 
 // float32 router: one thread per (token, expert), products and sums in
 // float64 in ascending h, bias added, rounded once to float32.
@@ -255,24 +274,27 @@ static void launch_topk(const moe_shape& s, const double* gsum, int ngroups, con
                        ids, w);
 }
 
-// The router logits, or (small bf16 batches) their group sums in `gsum`.
+// The router logits, or (bf16 batches up to 1024 tokens) their group sums
+// in `gsum`.
 static hipError_t launch_router(const moe_shape& s, const void* x, const void* w_router,
                                 const float* bias, float* lg, double* gsum, hipStream_t st) {
   if (s.act == MOE_DT_BF16) {
     const int np = router_parts(s.H);
-    if (gsum) {
-      dim3 grid((s.T + 15) / 16, (s.E + 15) / 16, router_groups(s.H));
-      hipLaunchKernelGGL(k_router_parts, grid, dim3(64 * kRouterGroup), 0, st,
-                         static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w_router),
-                         s.T, s.H, s.E, np, gsum);
+    const unsigned ng = gsum ? static_cast<unsigned>(router_groups(s.H)) : 1u;
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint16_t* wb = static_cast<const uint16_t*>(w_router);
+    if (s.T <= 64) {
+      dim3 grid((s.T + 15) / 16, (s.E + 15) / 16, ng);
+      hipLaunchKernelGGL(k_router_parts, grid, dim3(64 * kRouterGroup), 0, st, xb, wb, s.T, s.H,
+                         s.E, np, gsum);
     } else if (s.T <= 1024) {
-      dim3 grid((s.T + 31) / 32, (s.E + 31) / 32);
-      hipLaunchKernelGGL(k_router_lds<1>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x),
-                         static_cast<const uint16_t*>(w_router), bias, s.T, s.H, s.E, np, lg);
+      dim3 grid((s.T + 31) / 32, (s.E + 31) / 32, ng);
+      auto kern = gsum ? k_router_lds<1, true> : k_router_lds<1, false>;
+      hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, xb, wb, bias, s.T, s.H, s.E, np, lg, gsum);
     } else {
       dim3 grid((s.T + 63) / 64, (s.E + 63) / 64);
-      hipLaunchKernelGGL(k_router_lds<2>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(x),
-                         static_cast<const uint16_t*>(w_router), bias, s.T, s.H, s.E, np, lg);
+      hipLaunchKernelGGL((k_router_lds<2, false>), grid, dim3(256), 0, st, xb, wb, bias, s.T, s.H,
+                         s.E, np, lg, gsum);
     }
   } else {
     const size_t n = static_cast<size_t>(s.T) * s.E;
@@ -287,8 +309,8 @@ hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const
                         const float* bias, int32_t* ids, float* w, float* logits, void* ws,
                         hipStream_t st) {
   float* lg = logits ? logits : reinterpret_cast<float*>(static_cast<char*>(ws) + pl.logits_off);
-  double* gsum = router_small(s) ? reinterpret_cast<double*>(static_cast<char*>(ws) + pl.gsum_off)
-                                 : nullptr;
+  double* gsum = router_gsum(s) ? reinterpret_cast<double*>(static_cast<char*>(ws) + pl.gsum_off)
+                                : nullptr;
   hipError_t e = launch_router(s, x, w_router, bias, lg, gsum, st);
   if (e != hipSuccess) return e;
   const int nv = (s.E + 63) / 64, ng = router_groups(s.H);

@@ -54,7 +54,7 @@ bool make_plan(const moe_shape& s, Plan* p) {
   size_t off = 0;
   p->logits_off = off;
   off = align_up(off + static_cast<size_t>(T) * s.E * sizeof(float), 256);
-  if (router_small(s)) {
+  if (router_gsum(s)) {
     p->gsum_off = off;
     off = align_up(off + static_cast<size_t>(router_groups(s.H)) * T * s.E * sizeof(double), 256);
   }

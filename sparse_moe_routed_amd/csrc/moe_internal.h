@@ -15,7 +15,7 @@ namespace moe {
 struct Plan {
   // router
   size_t logits_off;      // float [T][E] (when the caller passes no logits buffer)
-  size_t gsum_off;        // double [router groups][T][E] (small bf16 batches)
+  size_t gsum_off;        // double [router groups][T][E] (bf16 batches up to 1024 tokens)
   // permutation
   int chunks;             // 256-token chunks of the large-batch path (0: one pass)
   size_t chunk_off;       // int32 chunk counts [chunks][E] + chunk bases [chunks][E]
@@ -46,7 +46,7 @@ struct PermPtrs {
 // Launchers: enqueue only, return hipGetLastError().
 int router_parts(int H);        // parts of the H reduction (largest divisor of H/32 <= 16)
 int router_groups(int H);       // groups of consecutive parts
-bool router_small(const moe_shape& s);   // router part sums finished by the top-k kernel
+bool router_gsum(const moe_shape& s);   // router group sums finished by the top-k kernel
 hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const void* w_router,
                         const float* bias, int32_t* ids, float* w, float* logits, void* ws,
                         hipStream_t st);

@@ -166,8 +166,10 @@ __global__ __launch_bounds__(1024) void k_permute_small(
 
 // Large batches: chunks of kChunkTok tokens.
 //   1) k_perm_count : per-chunk expert counts          (grid = chunks)
-//   2) k_perm_scan  : chunk bases, offsets, active, tiles (one workgroup)
-//   3) k_perm_place : stable rows inside each chunk     (grid = chunks)
+//   2) k_perm_scan  : chunk bases within each expert segment, offsets,
+//                     active, tiles (one workgroup)
+//   3) k_perm_place : stable rows (offset + chunk base + rank in chunk)
+//                     (grid = chunks)
 constexpr int kChunkTok = 256;
 constexpr int kChunkWords = kChunkTok / 32;
 
@@ -200,13 +202,21 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ 
   __shared__ int s_tot[17];
   const int tid = threadIdx.x;
   const int P = T * k;
+  // per expert: each chunk's first row relative to the expert's segment;
+  // the counts of a batch of chunks are loaded before any is added
+  constexpr int kScanBatch = 16;
   int run = 0;
   if (tid < E) {
-    for (int c = 0; c < nchunks; ++c) {
-      const size_t i = static_cast<size_t>(c) * E + tid;
-      const int v = chunk_cnt[i];
-      chunk_base[i] = run;
-      run += v;
+    for (int c0 = 0; c0 < nchunks; c0 += kScanBatch) {
+      int v[kScanBatch];
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u)
+        v[u] = c0 + u < nchunks ? chunk_cnt[static_cast<size_t>(c0 + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < kScanBatch; ++u) {
+        if (c0 + u < nchunks) chunk_base[static_cast<size_t>(c0 + u) * E + tid] = run;
+        run += v[u];
+      }
     }
     s_cnt[tid] = run;
   }
@@ -217,7 +227,6 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ 
     counts[tid] = run;
     offsets[tid] = ex;
     if (tid == E - 1) offsets[E] = ex + run;
-    for (int c = 0; c < nchunks; ++c) chunk_base[static_cast<size_t>(c) * E + tid] += ex;
   }
   const int flag = (tid < E && run > 0) ? 1 : 0;
   int nact = 0;
@@ -234,6 +243,7 @@ __global__ __launch_bounds__(1024) void k_perm_scan(const int32_t* __restrict__ 
 
 __global__ __launch_bounds__(1024) void k_perm_place(const int32_t* __restrict__ ids, int T, int k,
                                                      int E, const int32_t* __restrict__ chunk_base,
+                                                     const int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ sorted_pair,
                                                      int32_t* __restrict__ pair_row) {
   __shared__ uint32_t bits[1024 * kChunkWords];
@@ -255,7 +265,7 @@ __global__ __launch_bounds__(1024) void k_perm_place(const int32_t* __restrict__
     if (e < 0 || e >= E) continue;
     const int t = p / k - t0;
     const int wi = t >> 5;
-    int row = chunk_base[static_cast<size_t>(c) * E + e] +
+    int row = offsets[e] + chunk_base[static_cast<size_t>(c) * E + e] +
               __popc(bits[e * kChunkWords + wi] & ((1u << (t & 31)) - 1u));
     for (int w = 0; w < wi; ++w) row += __popc(bits[e * kChunkWords + w]);
     sorted_pair[row] = p;
@@ -315,6 +325,7 @@ hipError_t launch_permute(const moe_shape& s, const Plan& pl, const int32_t* ids
                        chunk_base, pp.counts, pp.offsets, pp.active, pp.n_active, rt, pl.max_tiles,
                        tiles);
     hipLaunchKernelGGL(k_perm_place, dim3(C), dim3(1024), 0, st, ids, s.T, s.top_k, s.E, chunk_base,
+                       pp.offsets,
                        pp.sorted_pair, pp.pair_row);
   }
   return hipGetLastError();

@@ -849,19 +849,20 @@ constexpr int tiled_mb_max() {
   return WF == WF_BF16 ? 2 : (NB >= 4 ? 2 : 4);
 }
 
-// bf16 gate/up with 16-row tiles (decode): one 16-row block of gate and of
-// up per wave with the next k unit's loads issued before the current one is
-// multiplied (unit_loop with PF).  Measured on the MI355X at 8 tokens: 77 us
-// against 80 us for two blocks per wave without it (and 78 us with one block
-// alone); the low-bit formats and taller tiles measured slower with it (the
+// bf16 with 16-row tiles (decode): one 16-row block per wave (of gate and
+// of up, or of down) with the next k unit's loads issued before the current
+// one is multiplied (unit_loop with PF).  Measured on the MI355X at 8 tokens:
+// gate/up 77 us against 80 us for two blocks per wave without it (78 us with
+// one block alone), the whole step 0.7% faster again with down done the same
+// way; the low-bit formats and taller tiles measured slower with it (the
 // second register stage halves their occupancy).
 template <int WF, int NB>
-constexpr bool gateup_pf() {
+constexpr bool tile_pf() {
   return WF == WF_BF16 && NB == 1;
 }
 template <int WF, int NB>
-constexpr int gateup_mb_max() {
-  return gateup_pf<WF, NB>() ? 1 : tiled_mb_max<WF, NB>();
+constexpr int tile_mb_max() {
+  return tile_pf<WF, NB>() ? 1 : tiled_mb_max<WF, NB>();
 }
 
 // largest MB <= mmax whose workgroup rows (rows_per_mb1 * MB) divide N
@@ -906,7 +907,7 @@ static void gateup_tiled_launch(const moe_shape& s, const Plan& pl, const void* 
                        pl.max_tiles, sorted_pair, s.top_k, s.H, s.I, s.T * s.top_k,
                        static_cast<uint16_t*>(h), min(o.band, pl.max_tiles), o.xcd);
   } else {
-    hipLaunchKernelGGL((k_gateup_t<WF, NB, KSPLIT, MB, gateup_pf<WF, NB>()>), item_grid(pl, nslices),
+    hipLaunchKernelGGL((k_gateup_t<WF, NB, KSPLIT, MB, tile_pf<WF, NB>()>), item_grid(pl, nslices),
                        dim3(256), 0, st, static_cast<const uint16_t*>(x),
                        static_cast<const uint8_t*>(ex.gate), static_cast<const uint8_t*>(ex.up),
                        ex.gate_scale, ex.up_scale, tiles, pl.max_tiles, sorted_pair, s.top_k, s.H,
@@ -919,7 +920,7 @@ template <int WF, int NB, int KSPLIT>
 static void gateup_tiled_mb(const moe_shape& s, const Plan& pl, const void* x,
                             const moe_experts& ex, const int32_t* sp, const int32_t* tiles,
                             void* h, hipStream_t st) {
-  constexpr int M = gateup_mb_max<WF, NB>();
+  constexpr int M = tile_mb_max<WF, NB>();
   switch (tiled_mb<WF, NB>(s.I, 16 * (4 / KSPLIT), M)) {
     case M: gateup_tiled_launch<WF, NB, KSPLIT, M>(s, pl, x, ex, sp, tiles, h, st); break;
     case (M > 1 ? M / 2 : 0):
@@ -969,7 +970,7 @@ static void down_tiled_launch(const moe_shape& s, const Plan& pl, const void* h,
                        ex.down_scale, tiles, pl.max_tiles, s.H, s.I, static_cast<uint16_t*>(y),
                        min(o.band, pl.max_tiles), o.xcd);
   } else {
-    hipLaunchKernelGGL((k_down_t<WF, NB, MB, false>), item_grid(pl, s.H / (64 * MB)),
+    hipLaunchKernelGGL((k_down_t<WF, NB, MB, tile_pf<WF, NB>()>), item_grid(pl, s.H / (64 * MB)),
                        dim3(256), 0, st, static_cast<const uint16_t*>(h),
                        static_cast<const uint8_t*>(ex.down), ex.down_scale, tiles, pl.max_tiles,
                        s.H, s.I, static_cast<uint16_t*>(y), min(o.band, pl.max_tiles), o.xcd);
@@ -980,7 +981,7 @@ template <int WF, int NB>
 static void launch_down_tiled(const moe_shape& s, const Plan& pl, const void* h,
                               const moe_experts& ex, const int32_t* tiles, void* y,
                               hipStream_t st) {
-  constexpr int M = tiled_mb_max<WF, NB>();
+  constexpr int M = tile_mb_max<WF, NB>();
   switch (tiled_mb<WF, NB>(s.H, 64, M)) {
     case M: down_tiled_launch<WF, NB, M>(s, pl, h, ex, tiles, y, st); break;
     case (M > 1 ? M / 2 : 0): down_tiled_launch<WF, NB, (M > 1 ? M / 2 : 1)>(s, pl, h, ex, tiles, y, st); break;

@@ -346,7 +346,15 @@ def main():
                      "flops_per_launch": round(avg_flops), "kernel_source_digest": digest,
                      "measured_read_GBps": probe,
                      "frac_of_measured": (round(achieved / probe, 4)
-                                          if probe and bound == "hbm" else None)},
+                                          if probe and bound == "hbm" else None),
+                     # both roofs for the same launches, and the attainable-roofline
+                     # fraction max(F / F_peak, B / B_peak) / t
+                     "hbm_frac": round(avg_bytes / (avg_ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "mfma_frac": round(avg_flops / (avg_ms / 1e3) / 1e12 /
+                                        (FP32_PEAK_TFLOPS if cfg.act == "f32" else BF16_PEAK_TFLOPS), 4),
+                     "attainable_frac": round(
+                         max(avg_flops / ((FP32_PEAK_TFLOPS if cfg.act == "f32" else BF16_PEAK_TFLOPS) * 1e12),
+                             avg_bytes / (HBM_PEAK_GBS * 1e9)) / (avg_ms / 1e3), 4)},
         "timing": {"mode": ("steps back to back" if not args.flush_mib else
                             f"{args.flush_mib} MiB scratch read between steps, excluded"),
                    "step_ms_median": round(float(np.median(step_ms)), 5),

@@ -73,6 +73,52 @@ def parse():
     return ap.parse_args()
 
 
+class TimingEvent:
+    """A HIP event used only for timing: created with hipEventDisableSystemFence,
+    so recording it does not write back and invalidate the caches (a default
+    timing event costs the step about 3 us of GPU time per record on the
+    MI355X).  Recorded on torch's current stream unless a stream is given."""
+
+    FLAGS = 0x20000000          # hipEventDisableSystemFence
+    _hip = None
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            import ctypes
+            h = ctypes.CDLL("libamdhip64.so")
+            vp = ctypes.c_void_p
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [vp, vp]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            h.hipEventDestroy.argtypes = [vp]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self.ev = ctypes.c_void_p()
+        if self.hip().hipEventCreateWithFlags(ctypes.byref(self.ev), self.FLAGS) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream=None):
+        import torch
+        st = (stream or torch.cuda.current_stream()).cuda_stream
+        if self.hip().hipEventRecord(self.ev, st) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end) -> float:
+        import ctypes
+        ms = ctypes.c_float()
+        if self.hip().hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
+
+
 def weight_bytes_per_param(cfg):
     if cfg.wfmt == "dense":
         return 4.0 if cfg.act == "f32" else 2.0
@@ -195,8 +241,8 @@ def main():
     acts = [torch.empty_like(xs[0]) for _ in range(2)]
     torch.cuda.synchronize()
 
-    ev_a = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * L)]
-    ev_b = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps * L)]
+    ev_a = [TimingEvent() for _ in range(args.steps * L)]
+    ev_b = [TimingEvent() for _ in range(args.steps * L)]
 
     def step(i, timed_idx=None):
         x = xs[i % len(xs)]
@@ -241,8 +287,8 @@ def main():
     torch.cuda.synchronize()
     # one event at every step boundary (plus one after each step when
     # flushing, so that the flush is outside the step times)
-    ev_beg = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    ev_end = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)] if args.flush_mib else None
+    ev_beg = [TimingEvent() for _ in range(args.steps + 1)]
+    ev_end = [TimingEvent() for _ in range(args.steps)] if args.flush_mib else None
     scratch = sink = None
     if args.flush_mib:
         scratch = torch.zeros(args.flush_mib << 20, dtype=torch.uint8, device=dev)
@@ -295,7 +341,7 @@ def main():
     step_bytes = np.mean([sum(layer_bytes(cfg, U[b, l]) for l in range(L)) for b in range(len(xs))])
     graph = None if args.no_graph else graph_replay(torch, buf, layers, xs, acts, cfg, L, args.steps)
     # route-locality kernel time (on the last routes)
-    la, lb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    la, lb = TimingEvent(), TimingEvent()
     buf.route_locality()
     la.record()
     for _ in range(20):
@@ -401,7 +447,7 @@ def graph_replay(torch, buf, layers, xs, acts, cfg, L, steps):
         torch.cuda.synchronize()
         for i in range(3):
             graphs[i % len(graphs)].replay()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         torch.cuda.synchronize()
         a.record()
         for i in range(steps):
@@ -461,7 +507,7 @@ def offload(M, torch, dev, cfg, layers, xs, buf, steps):
             for i in range(2):
                 one(xs[i % len(xs)], split)
             torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a, b = TimingEvent(), TimingEvent()
             a.record()
             for i in range(steps):
                 one(xs[i % len(xs)], split)
@@ -482,7 +528,7 @@ def offload(M, torch, dev, cfg, layers, xs, buf, steps):
         all_active = torch.arange(cfg.E, dtype=torch.int32, device=dev)
         n_all = torch.full((1,), cfg.E, dtype=torch.int32, device=dev)
         allp = M.make_perm(buf.counts, buf.offsets, buf.sorted_pair, buf.pair_row, all_active, n_all)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         M.moe_stage_experts(buf.shape, src_s, dst_s, allp)
         torch.cuda.synchronize()
         a.record()
@@ -534,7 +580,7 @@ def fused_waves(M, torch, dev, cfg, layers, xs, reps=50):
             for i in range(5):
                 fn(i)
             torch.cuda.synchronize()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a, b = TimingEvent(), TimingEvent()
             a.record()
             for i in range(reps):
                 fn(i)
@@ -592,7 +638,7 @@ def read_probe(M, dev, mib):
         M.moe_stream_read(buf, n, sink)
     ms = []
     for _ in range(5):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record()
         M.moe_stream_read(buf, n, sink)
         b.record()

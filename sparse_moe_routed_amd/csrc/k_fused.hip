@@ -28,10 +28,7 @@
 
 namespace moe {
 
-constexpr int kFusedCols = 64;              // intermediate columns per work item
 constexpr int kHsStride = kFusedCols + 8;   // LDS row stride of h in bf16 (padded)
-
-int fused_slices(const moe_shape& s) { return s.I / kFusedCols; }
 
 // One workgroup of 4 waves per item.  Gate/up: wave w owns intermediate
 // columns 16w .. 16w+15 of the slice for gate and for up over the full K = H,

@@ -170,7 +170,6 @@ __global__ __launch_bounds__(1024) void k_permute_small(
 //                     active, tiles (one workgroup)
 //   3) k_perm_place : stable rows (offset + chunk base + rank in chunk)
 //                     (grid = chunks)
-constexpr int kChunkTok = 256;
 constexpr int kChunkWords = kChunkTok / 32;
 
 __global__ __launch_bounds__(1024) void k_perm_count(const int32_t* __restrict__ ids, int T, int k,
@@ -300,12 +299,6 @@ __global__ __launch_bounds__(1024) void k_plan_tiles(const int32_t* __restrict__
   __syncthreads();
   emit_tiles(nact, s_act, s_cnt, s_off, P, rt, max_tiles, tiles, s_tot);
 }
-
-bool permute_single_pass(const moe_shape& s) {
-  return static_cast<size_t>(s.E) * ((s.T + 31) / 32) * 2 * sizeof(uint32_t) <= 48 * 1024;
-}
-
-int permute_chunks(const moe_shape& s) { return (s.T + kChunkTok - 1) / kChunkTok; }
 
 hipError_t launch_permute(const moe_shape& s, const Plan& pl, const int32_t* ids,
                           const PermPtrs& pp, int32_t* tiles, void* ws, hipStream_t st) {

@@ -160,25 +160,6 @@ __global__ __launch_bounds__(256) void k_router_lds(const uint16_t* __restrict__
   }
 }
 
-int router_parts(int H) {
-  const int chunks = H / 32;
-  int best = 1;
-  for (int d = 1; d <= kRouterMaxParts; ++d)
-    if (chunks % d == 0) best = d;
-  return best;
-}
-
-int router_groups(int H) { return (router_parts(H) + kRouterGroup - 1) / kRouterGroup; }
-
-// Token limit of the group-sum path: one workgroup per group of parts
-// multiplies the parallelism of the router by the group count (512 tokens:
-// 3.7 us less per layer); at 4096 tokens the float64 group sums (groups *
-// T * E * 8 bytes = 64 MB) cost more than the parallelism saves (+13 us),
-// so larger batches let the LDS kernel finish the sums.
-constexpr int kRouterGsumMaxT = 1024;
-
-bool router_gsum(const moe_shape& s) { return s.act == MOE_DT_BF16 && s.T <= kRouterGsumMaxT; }
-
 // float32 router: one thread per (token, expert), products and sums in
 // float64 in ascending h, bias added, rounded once to float32.
 __global__ __launch_bounds__(256) void k_router_f32(const float* __restrict__ x,

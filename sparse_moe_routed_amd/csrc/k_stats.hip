@@ -9,14 +9,6 @@
 
 namespace moe {
 
-constexpr int kMaxLocalityBlock = 5;
-
-int locality_blocks(int T) {
-  int n = 0;
-  for (int B = 1; B <= kMaxLocalityBlock; ++B) n += (T + B - 1) / B;
-  return n;
-}
-
 // One wave per output value: overlap of token t (outputs 0..T-1), then the
 // block unions (B = 1..5 in turn).  The wave copies the ids it needs (tokens
 // t-1 and t, or the block's tokens: at most 5 top_k values) into LDS, each

@@ -3,7 +3,7 @@
 // point, so a rejected call enqueues nothing and writes nothing (the
 // fail-closed admission rule of "Agent Field Notes -- full corpus", AFN-001,
 // section "Phase 3: reject before the GPU exists").
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <algorithm>
 #include <cstdint>

@@ -2,13 +2,22 @@
 // launchers.  Nothing here is exported.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stddef.h>
 #include <stdint.h>
 
 #include "../../include/moe.h"
 
 namespace moe {
+
+// Sizes shared by the host planning code (plan.cpp) and the kernels.
+constexpr int kChunkTok = 256;          // tokens per chunk of the large-batch permutation
+constexpr int kRouterGroup = 4;         // consecutive H parts whose sums are added first
+constexpr int kRouterMaxParts = 16;     // parts of the router's H reduction, at most
+constexpr int kRouterMaxGroups = kRouterMaxParts / kRouterGroup;
+constexpr int kRouterGsumMaxT = 1024;   // group sums finished by the top-k kernel up to here
+constexpr int kFusedCols = 64;          // intermediate columns per fused-FFN work item
+constexpr int kMaxLocalityBlock = 5;    // route-locality block sizes 1..5
 
 // Launch geometry and workspace layout for one shape.  Every region is
 // 256-byte aligned; moe_workspace_size() returns `total`.

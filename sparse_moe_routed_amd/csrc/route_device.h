@@ -8,13 +8,11 @@
 #pragma once
 
 #include "moe_device.h"
+#include "moe_internal.h"
 
 namespace moe {
 
 constexpr int kRouterBatch = 8;
-constexpr int kRouterGroup = 4;       // consecutive H parts whose sums are added first
-constexpr int kRouterMaxParts = 16;
-constexpr int kRouterMaxGroups = kRouterMaxParts / kRouterGroup;
 
 // One part of a 16-token x 16-expert logit tile, by one wave: float32
 // chunk sums from MFMA, added in float64 in k order.  slot[lane][j]

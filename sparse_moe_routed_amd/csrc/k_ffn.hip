@@ -561,17 +561,12 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
 // gate/up + SwiGLU, KSPLIT = 1: each wave owns MB 16-row blocks of gate and
 // of up (64 MB rows per workgroup) over the full K = H.  1-D grid over
 // (tile, slice) items, block 256.
-template <int WF, int NB, int MB>
-__global__ __launch_bounds__(256) void k_gateup_x(
+template <int WF, int NB, int MB, int AUX>
+__device__ __forceinline__ void gateup_x_body(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
-    const uint16_t* __restrict__ sg, const uint16_t* __restrict__ su,
-    const int32_t* __restrict__ tiles, int max_tiles, const int32_t* __restrict__ sorted_pair,
-    int k, int H, int I, int P, uint16_t* __restrict__ h, int band, int xcd) {
-  __shared__ __align__(16) char xs[2][NB * 4096];
-  int ti, sl;
-  if (!tile_item(tiles[3 * max_tiles], I / (64 * MB), band, xcd != 0, ti, sl)) return;
-  const Tile tl = read_tile(tiles, ti);
-  if (tl.rows <= 0) return;
+    const uint16_t* __restrict__ sg, const uint16_t* __restrict__ su, const Tile tl, int sl,
+    const int32_t* __restrict__ sorted_pair, int k, int H, int I, int P,
+    uint16_t* __restrict__ h, char (*xs)[NB * 4096]) {
   // wave index as a uniform value (the slab base below must live in SGPRs)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
@@ -605,14 +600,14 @@ __global__ __launch_bounds__(256) void k_gateup_x(
     if constexpr (WF != WF_BF16) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        sc[mb][0] = tscales<WF, weight_aux<NB>()>(Sg, mb, u, r);
-        sc[mb][1] = tscales<WF, weight_aux<NB>()>(Su, mb, u, r);
+        sc[mb][0] = tscales<WF, AUX>(Sg, mb, u, r);
+        sc[mb][1] = tscales<WF, AUX>(Su, mb, u, r);
       }
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-      raw[mb][0] = tload<WF, weight_aux<NB>()>(Sg, mb, u, lane);
-      raw[mb][1] = tload<WF, weight_aux<NB>()>(Su, mb, u, lane);
+      raw[mb][0] = tload<WF, AUX>(Sg, mb, u, lane);
+      raw[mb][1] = tload<WF, AUX>(Su, mb, u, lane);
     }
     if (u + 1 < units) xu.load(u + 1);
     SCHED_FENCE();
@@ -667,19 +662,40 @@ __global__ __launch_bounds__(256) void k_gateup_x(
   }
 }
 
-// down with the intermediate rows staged through LDS (same scheme, K = I).
+// The weight cache policy per tile: an expert with a single tile reads its
+// records once in this call, so they stream non-temporal like the small-tile
+// kernels' loads; the tiles of experts with several tiles keep the default
+// policy, so their shared slices stay in L2 for the neighbouring items.
+__device__ __forceinline__ bool single_tile(const int32_t* __restrict__ tiles, int max_tiles, int ti,
+                                            int e) {
+  const int n = tiles[3 * max_tiles];
+  return (ti == 0 || tiles[3 * (ti - 1)] != e) && (ti + 1 >= n || tiles[3 * (ti + 1)] != e);
+}
+
 template <int WF, int NB, int MB>
-__global__ __launch_bounds__(256) void k_down_x(const uint16_t* __restrict__ h,
-                                                const uint8_t* __restrict__ wd,
-                                                const uint16_t* __restrict__ sd,
-                                                const int32_t* __restrict__ tiles, int max_tiles,
-                                                int H, int I, uint16_t* __restrict__ y, int band,
-                                                int xcd) {
+__global__ __launch_bounds__(256) void k_gateup_x(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
+    const uint16_t* __restrict__ sg, const uint16_t* __restrict__ su,
+    const int32_t* __restrict__ tiles, int max_tiles, const int32_t* __restrict__ sorted_pair,
+    int k, int H, int I, int P, uint16_t* __restrict__ h, int band, int xcd) {
   __shared__ __align__(16) char xs[2][NB * 4096];
   int ti, sl;
-  if (!tile_item(tiles[3 * max_tiles], H / (64 * MB), band, xcd != 0, ti, sl)) return;
+  if (!tile_item(tiles[3 * max_tiles], I / (64 * MB), band, xcd != 0, ti, sl)) return;
   const Tile tl = read_tile(tiles, ti);
   if (tl.rows <= 0) return;
+  if (single_tile(tiles, max_tiles, ti, tl.e))
+    gateup_x_body<WF, NB, MB, kWeightAux>(x, wg, wu, sg, su, tl, sl, sorted_pair, k, H, I, P, h, xs);
+  else
+    gateup_x_body<WF, NB, MB, 0>(x, wg, wu, sg, su, tl, sl, sorted_pair, k, H, I, P, h, xs);
+}
+
+// down with the intermediate rows staged through LDS (same scheme, K = I).
+template <int WF, int NB, int MB, int AUX>
+__device__ __forceinline__ void down_x_body(const uint16_t* __restrict__ h,
+                                            const uint8_t* __restrict__ wd,
+                                            const uint16_t* __restrict__ sd, const Tile tl, int sl,
+                                            int H, int I, uint16_t* __restrict__ y,
+                                            char (*xs)[NB * 4096]) {
   // wave index as a uniform value (the slab base below must live in SGPRs)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
@@ -706,10 +722,10 @@ __global__ __launch_bounds__(256) void k_down_x(const uint16_t* __restrict__ h,
     TRaw<WF> raw[MB];
     if constexpr (WF != WF_BF16) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) sc[mb] = tscales<WF, weight_aux<NB>()>(Sd, mb, u, r);
+      for (int mb = 0; mb < MB; ++mb) sc[mb] = tscales<WF, AUX>(Sd, mb, u, r);
     }
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) raw[mb] = tload<WF, weight_aux<NB>()>(Sd, mb, u, lane);
+    for (int mb = 0; mb < MB; ++mb) raw[mb] = tload<WF, AUX>(Sd, mb, u, lane);
     if (u + 1 < units) xu.load(u + 1);
     SCHED_FENCE();
     const char* buf = xs[u & 1];
@@ -759,6 +775,24 @@ __global__ __launch_bounds__(256) void k_down_x(const uint16_t* __restrict__ h,
 
 // float32 path (act and weights float32): one thread per output, float32
 // fused multiply-adds in ascending k.  grid (max_tiles, ceil(N/16)),
+template <int WF, int NB, int MB>
+__global__ __launch_bounds__(256) void k_down_x(const uint16_t* __restrict__ h,
+                                                const uint8_t* __restrict__ wd,
+                                                const uint16_t* __restrict__ sd,
+                                                const int32_t* __restrict__ tiles, int max_tiles,
+                                                int H, int I, uint16_t* __restrict__ y, int band,
+                                                int xcd) {
+  __shared__ __align__(16) char xs[2][NB * 4096];
+  int ti, sl;
+  if (!tile_item(tiles[3 * max_tiles], H / (64 * MB), band, xcd != 0, ti, sl)) return;
+  const Tile tl = read_tile(tiles, ti);
+  if (tl.rows <= 0) return;
+  if (single_tile(tiles, max_tiles, ti, tl.e))
+    down_x_body<WF, NB, MB, kWeightAux>(h, wd, sd, tl, sl, H, I, y, xs);
+  else
+    down_x_body<WF, NB, MB, 0>(h, wd, sd, tl, sl, H, I, y, xs);
+}
+
 // block 256 = 16 rows x 16 outputs.
 __global__ __launch_bounds__(256) void k_gateup_f32(const float* __restrict__ x,
                                                     const float* __restrict__ wg,

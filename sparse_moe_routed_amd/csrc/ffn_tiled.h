@@ -108,9 +108,10 @@ struct TRaw {
 // once per call, so it is read non-temporal (bit 1 -> `nt` on gfx950): a
 // streaming read of 4 GiB measured 7.0 TB/s with `nt` against 6.2 TB/s
 // without, and the decode FFN gained 6%.  With 64-row tiles (large batches)
-// hot experts' slices are read again by their other tiles from L2; `nt`
-// there cost 12% (4096 tokens) to 31% (32768 tokens), so those loads keep
-// the default policy.
+// hot experts' slices are read again by their other tiles from L2; `nt` on
+// every tile there cost 12% (4096 tokens) to 31% (32768 tokens), so the
+// large-batch kernels choose per tile: `nt` only for an expert with a single
+// tile (single_tile in the FFN kernels; +2.6% at 4096 tokens).
 constexpr int kWeightAux = 2;
 template <int NB>
 constexpr int weight_aux() {

@@ -165,6 +165,14 @@ __device__ __forceinline__ TRaw<WF> tload(const Slab<WF>& S, int mb, int kb, int
   return t;
 }
 
+// bf16: fragment f (k chunk f) of row block mb, k unit kb.
+template <int AUX>
+__device__ __forceinline__ u32x4_t tload_frag(const Slab<WF_BF16>& S, int mb, int kb, int f,
+                                              int lane) {
+  return __builtin_amdgcn_raw_buffer_load_b128(S.w, lane * 16 + f * 1024,
+                                               (mb * (S.K / 32) + 4 * kb) * 1024, AUX);
+}
+
 template <int WF>
 __device__ __forceinline__ Dq dq_consts() {
   if constexpr (WF == WF_BF16) return Dq{0u, 0u};   // unused

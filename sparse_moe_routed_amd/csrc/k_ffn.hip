@@ -939,13 +939,17 @@ static void launch_down_wf(const moe_shape& s, const Plan& pl, const void* h,
 
 // Rows per wave (16 MB) for the tiled kernels: bf16 keeps 32 rows (the raw
 // fragments are 64 B per lane per row block); low-bit formats take 64 rows
-// (32 at 64-row token tiles) so that every token fragment feeds more MFMAs.
+// so that every token fragment feeds more MFMAs, except at 64-row token
+// tiles: there gate/up takes 16 rows (of gate and of up) and down 32.
 // Measured on MI355X: 128 rows (int2 at 16-row tiles) leaves too few waves
 // to hide the dequant work (24 -> 28 us per 48-layer verify gate/up launch);
-// every launched variant stays within the register budget without spills.
-template <int WF, int NB>
+// the 32-row low-bit gate/up at 64-row tiles needed 256 VGPRs + 150 AGPRs
+// (one wave per SIMD), the 16-row one fits 228 (two): 1074 -> 738 us (int4)
+// and 954 -> 633 us (int2) per gate/up launch at 4096 tokens; down at 16
+// rows was slower (its 32-row form already runs two waves per SIMD).
+template <int WF, int NB, bool GATEUP>
 constexpr int tiled_mb_max() {
-  return WF == WF_BF16 ? 2 : (NB >= 4 ? 2 : 4);
+  return WF == WF_BF16 ? 2 : (NB >= 4 ? (GATEUP ? 1 : 2) : 4);
 }
 
 // bf16 with 16-row tiles (decode): one 16-row block per wave (of gate and
@@ -968,9 +972,9 @@ template <int WF, bool GATEUP>
 constexpr bool x_roll() {
   return WF == WF_BF16 && GATEUP;
 }
-template <int WF, int NB>
+template <int WF, int NB, bool GATEUP>
 constexpr int tile_mb_max() {
-  return tile_pf<WF, NB>() ? 1 : tiled_mb_max<WF, NB>();
+  return tile_pf<WF, NB>() ? 1 : tiled_mb_max<WF, NB, GATEUP>();
 }
 
 // largest MB <= mmax whose workgroup rows (rows_per_mb1 * MB) divide N
@@ -1028,7 +1032,7 @@ template <int WF, int NB, int KSPLIT>
 static void gateup_tiled_mb(const moe_shape& s, const Plan& pl, const void* x,
                             const moe_experts& ex, const int32_t* sp, const int32_t* tiles,
                             void* h, hipStream_t st) {
-  constexpr int M = tile_mb_max<WF, NB>();
+  constexpr int M = tile_mb_max<WF, NB, true>();
   switch (tiled_mb<WF, NB>(s.I, 16 * (4 / KSPLIT), M)) {
     case M: gateup_tiled_launch<WF, NB, KSPLIT, M>(s, pl, x, ex, sp, tiles, h, st); break;
     case (M > 1 ? M / 2 : 0):
@@ -1089,7 +1093,7 @@ template <int WF, int NB>
 static void launch_down_tiled(const moe_shape& s, const Plan& pl, const void* h,
                               const moe_experts& ex, const int32_t* tiles, void* y,
                               hipStream_t st) {
-  constexpr int M = tile_mb_max<WF, NB>();
+  constexpr int M = tile_mb_max<WF, NB, false>();
   switch (tiled_mb<WF, NB>(s.H, 64, M)) {
     case M: down_tiled_launch<WF, NB, M>(s, pl, h, ex, tiles, y, st); break;
     case (M > 1 ? M / 2 : 0): down_tiled_launch<WF, NB, (M > 1 ? M / 2 : 1)>(s, pl, h, ex, tiles, y, st); break;

@@ -30,6 +30,8 @@ SMALL = {
     "int4_small": C4.with_(T=96, H=512, E=64, I=128, k=8, layers=1),
     "int2_small": C5.with_(T=16, H=512, E=64, I=128, layers=1),
     "int4_many_rows": C4.with_(T=1500, H=256, E=16, I=128, k=4, layers=1),
+    # low-bit 64-row tiles with 6 gate/up slices of 16 rows per wave
+    "int2_many_rows": C5.with_(T=1300, H=256, E=16, I=384, k=4, layers=1, bias="none"),
     "int2_ksplit_rows": C5.with_(T=600, H=384, E=24, I=96, k=3, layers=1, bias="none"),
     # LDS-staged router with a ragged expert tile and parts that end inside
     # a 128-wide k unit (H/32 = 20 chunks, 10 parts of 2)

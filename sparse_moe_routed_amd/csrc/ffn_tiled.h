@@ -92,6 +92,16 @@ __device__ __forceinline__ bool tile_item(int n_tiles, int nslices, int band, bo
   return true;
 }
 
+// The weight cache policy per tile: an expert with a single tile reads its
+// records once in this call, so they stream non-temporal like the small-tile
+// kernels' loads; the tiles of experts with several tiles keep the default
+// policy, so their shared slices stay in L2 for the neighbouring items.
+__device__ __forceinline__ bool single_tile(const int32_t* __restrict__ tiles, int max_tiles, int ti,
+                                            int e) {
+  const int n = tiles[3 * max_tiles];
+  return (ti == 0 || tiles[3 * (ti - 1)] != e) && (ti + 1 >= n || tiles[3 * (ti + 1)] != e);
+}
+
 // ---------------------------------------------------------------------------
 // Tiled weights (MOE_F_TILED_WEIGHTS).  The unit of the k loop is 128 k = 4
 // MFMA chunks; for one 16-row block a lane fetches, per unit, 4 x 16 B (bf16:

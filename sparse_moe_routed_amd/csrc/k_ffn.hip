@@ -674,36 +674,42 @@ __device__ __forceinline__ void gateup_x_body(
       }
     }
   }, [&](const Stage& w, const char* buf, int f) {
-    // bf16: k chunk f; low-bit: all four k chunks of the unit
-    constexpr int NS = WF == WF_BF16 ? 1 : 4;
+    if constexpr (WF == WF_BF16) {
+      // k chunk f, token blocks outer: one token fragment is live at a time
+      // (what lets 128-row tiles fit 256 VGPRs)
 #pragma unroll
-    for (int s4 = 0; s4 < NS; ++s4) {
-      const int st = WF == WF_BF16 ? f : s4;
+      for (int b = 0; b < NB; ++b) {
+        const u32x4_t xa = xfrag<NB>(buf, f, b, lane);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int gu = 0; gu < 2; ++gu)
+            acc[mb][gu][b] = mfma_bf16(xa, w.raw[mb][gu].v[f], acc[mb][gu][b]);
+      }
+      return;
+    }
+    // low-bit: all four k chunks of the unit
+    constexpr int NS = 4;
+#pragma unroll
+    for (int st = 0; st < NS; ++st) {
       u32x4_t xa[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) xa[b] = xfrag<NB>(buf, st, b, lane);
       f32x4_t corr[NB];
-      if constexpr (WF != WF_BF16) {
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
-          corr[b] = mfma_bf16(xa[b], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
-      }
+      for (int b = 0; b < NB; ++b)
+        corr[b] = mfma_bf16(xa[b], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
         for (int gu = 0; gu < 2; ++gu) {
           const u32x4_t wv = tdecode<WF>(w.raw[mb][gu], st, dq);
-          if constexpr (WF == WF_BF16) {
+          const float sv = fp16_to_f32(w.sc[mb][gu].s[st]);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) acc[mb][gu][b] = mfma_bf16(xa[b], wv, acc[mb][gu][b]);
-          } else {
-            const float sv = fp16_to_f32(w.sc[mb][gu].s[st]);
+          for (int b = 0; b < NB; ++b) {
+            const f32x4_t pp = mfma_bf16(xa[b], wv, corr[b]);
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-              const f32x4_t pp = mfma_bf16(xa[b], wv, corr[b]);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) acc[mb][gu][b][j] = fmaf(sv, pp[j], acc[mb][gu][b][j]);
-            }
+            for (int j = 0; j < 4; ++j) acc[mb][gu][b][j] = fmaf(sv, pp[j], acc[mb][gu][b][j]);
           }
         }
       }
@@ -723,16 +729,6 @@ __device__ __forceinline__ void gateup_x_body(
               f32_to_bf16(silu(acc[mb][0][b][j]) * acc[mb][1][b][j]);
       }
   }
-}
-
-// The weight cache policy per tile: an expert with a single tile reads its
-// records once in this call, so they stream non-temporal like the small-tile
-// kernels' loads; the tiles of experts with several tiles keep the default
-// policy, so their shared slices stay in L2 for the neighbouring items.
-__device__ __forceinline__ bool single_tile(const int32_t* __restrict__ tiles, int max_tiles, int ti,
-                                            int e) {
-  const int n = tiles[3 * max_tiles];
-  return (ti == 0 || tiles[3 * (ti - 1)] != e) && (ti + 1 >= n || tiles[3 * (ti + 1)] != e);
 }
 
 template <int WF, int NB, int MB, bool ROLL>
@@ -846,13 +842,19 @@ __global__ __launch_bounds__(256) void k_down_x(const uint16_t* __restrict__ h,
                                                 const uint16_t* __restrict__ sd,
                                                 const int32_t* __restrict__ tiles, int max_tiles,
                                                 int H, int I, uint16_t* __restrict__ y, int band,
-                                                int xcd) {
+                                                int xcd, int split) {
   __shared__ __align__(16) char xs[2][NB * 4096];
-  int ti, sl;
-  if (!tile_item(tiles[3 * max_tiles], H / (64 * MB), band, xcd != 0, ti, sl)) return;
-  const Tile tl = read_tile(tiles, ti);
+  int vt, sl;
+  if (!tile_item(tiles[3 * max_tiles] * split, H / (64 * MB), band, xcd != 0, vt, sl)) return;
+  // plan tiles taller than 16 NB rows are taken in `split` parts of 16 NB rows
+  const int ti = vt / split, part = vt % split;
+  Tile tl = read_tile(tiles, ti);
+  // non-temporal weight loads only where this item is the expert's only one
+  const bool single = single_tile(tiles, max_tiles, ti, tl.e) && tl.rows <= 16 * NB;
+  tl.row0 += part * 16 * NB;
+  tl.rows = min(tl.rows - part * 16 * NB, 16 * NB);
   if (tl.rows <= 0) return;
-  if (single_tile(tiles, max_tiles, ti, tl.e))
+  if (single)
     down_x_body<WF, NB, MB, kWeightAux, ROLL>(h, wd, sd, tl, sl, H, I, y, xs);
   else
     down_x_body<WF, NB, MB, 0, ROLL>(h, wd, sd, tl, sl, H, I, y, xs);
@@ -1056,6 +1058,12 @@ static void launch_gateup_tiled(const moe_shape& s, const Plan& pl, const void* 
 template <int WF>
 static void gateup_nb(const moe_shape& s, const Plan& pl, const void* x, const moe_experts& ex,
                       const int32_t* sp, const int32_t* tiles, void* h, hipStream_t st) {
+  if constexpr (WF == WF_BF16) {
+    if (pl.nb == 8) {   // bf16 tiled only (plan_nb)
+      launch_gateup_tiled<WF, 8>(s, pl, x, ex, sp, tiles, h, st);
+      return;
+    }
+  }
   if (s.flags & MOE_F_TILED_WEIGHTS) {
     switch (pl.nb) {
       case 1: launch_gateup_tiled<WF, 1>(s, pl, x, ex, sp, tiles, h, st); break;
@@ -1077,10 +1085,15 @@ static void down_tiled_launch(const moe_shape& s, const Plan& pl, const void* h,
                               hipStream_t st) {
   const TileOrder o = tile_order(pl, false);
   if constexpr (NB >= 4) {
-    hipLaunchKernelGGL((k_down_x<WF, NB, MB, x_roll<WF, false>()>), item_grid(pl, s.H / (64 * MB)), dim3(256), 0, st,
+    // 128-row plan tiles run as two 64-row halves (measured: the 128-row down
+    // kernel, 188 VGPRs, was slower than two 64-row items)
+    const int split = pl.nb / NB;
+    const int64_t n = static_cast<int64_t>(pl.max_tiles) * split * (s.H / (64 * MB));
+    hipLaunchKernelGGL((k_down_x<WF, NB, MB, x_roll<WF, false>()>),
+                       dim3(static_cast<unsigned>((n + 7) / 8 * 8)), dim3(256), 0, st,
                        static_cast<const uint16_t*>(h), static_cast<const uint8_t*>(ex.down),
                        ex.down_scale, tiles, pl.max_tiles, s.H, s.I, static_cast<uint16_t*>(y),
-                       min(o.band, pl.max_tiles), o.xcd);
+                       min(o.band, pl.max_tiles * split), o.xcd, split);
   } else {
     hipLaunchKernelGGL((k_down_t<WF, NB, MB, tile_pf<WF, NB>()>), item_grid(pl, s.H / (64 * MB)),
                        dim3(256), 0, st, static_cast<const uint16_t*>(h),
@@ -1104,6 +1117,12 @@ static void launch_down_tiled(const moe_shape& s, const Plan& pl, const void* h,
 template <int WF>
 static void down_nb(const moe_shape& s, const Plan& pl, const void* h, const moe_experts& ex,
                     const int32_t* tiles, void* y, hipStream_t st) {
+  if constexpr (WF == WF_BF16) {
+    if (pl.nb == 8) {   // bf16 tiled only (plan_nb): 64-row halves of the 128-row tiles
+      launch_down_tiled<WF, 4>(s, pl, h, ex, tiles, y, st);
+      return;
+    }
+  }
   if (s.flags & MOE_F_TILED_WEIGHTS) {
     switch (pl.nb) {
       case 1: launch_down_tiled<WF, 1>(s, pl, h, ex, tiles, y, st); break;

@@ -71,6 +71,8 @@ hipError_t launch_gateup(const moe_shape& s, const Plan& pl, const void* x, cons
                          hipStream_t st);
 hipError_t launch_down(const moe_shape& s, const Plan& pl, const void* h, const moe_experts& ex,
                        const int32_t* tiles, void* y, hipStream_t st);
+// 128-row tiles (nb = 8) are planned only for bf16 tiled weights
+bool tiles128_ok(const moe_shape& s);
 hipError_t launch_ffn(const moe_shape& s, const Plan& pl, const void* x, const moe_experts& ex,
                       const int32_t* sorted_pair, const int32_t* tiles, void* h, void* y,
                       hipStream_t st);

@@ -30,7 +30,7 @@ SMALL = {
     "int4_small": C4.with_(T=96, H=512, E=64, I=128, k=8, layers=1),
     "int2_small": C5.with_(T=16, H=512, E=64, I=128, layers=1),
     "int4_many_rows": C4.with_(T=1500, H=256, E=16, I=128, k=4, layers=1),
-    # 128-row tiles (T*k >= 256 E, bf16 tiled): gate/up at 16 token blocks,
+    # 128-row tiles (T*k >= 48 E, bf16 tiled): gate/up at 8 token blocks,
     # down on 64-row halves; ragged tails, experts with 0..1883 rows, 2 and 3
     # gate/up slices, 2 and 5 k units
     "bf16_tiles128": C3.with_(T=2050, H=256, E=16, I=256, k=2),

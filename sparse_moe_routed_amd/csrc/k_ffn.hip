@@ -614,6 +614,40 @@ __device__ __forceinline__ void staged_loop(int units, XU& xu, char (*xs)[NB * 4
   }
 }
 
+// The bf16 output tile of an LDS-staged item -- rows 0 .. 16 NB - 1 of the
+// tile, columns col0 .. col0 + 64 MB - 1 -- written through LDS: value(mb, b,
+// j) of lane (r, q) in wave w is row 16 b + 4 q + j, column 16 (MB w + mb) +
+// r, so direct stores would be 2-byte scatters (4 MB NB per lane); staged,
+// each thread stores 16 contiguous bytes.  `lds` holds the tile (row pitch
+// 128 MB + 16 bytes); the caller's k loop is done with it.
+template <int NB, int MB, typename Val>
+__device__ __forceinline__ void store_tile(char* lds, Val&& val, int rows,
+                                           uint16_t* __restrict__ dst, size_t ld, int col0) {
+  constexpr int pitch = 128 * MB + 16;
+  static_assert(16 * NB * pitch <= 2 * NB * 4096, "output tile exceeds the staging buffers");
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, q = lane >> 4;
+  __syncthreads();   // every wave is done reading the token units
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint16_t*>(lds + (16 * b + 4 * q + j) * pitch +
+                                     (16 * (MB * wave + mb) + r) * 2) = f32_to_bf16(val(mb, b, j));
+  __syncthreads();
+  constexpr int segs = 8 * MB;   // 16-byte segments per row
+#pragma unroll
+  for (int it = 0; it < NB * MB / 2; ++it) {
+    const int g = it * 256 + static_cast<int>(threadIdx.x);
+    const int row = g / segs, cs = g % segs;
+    if (row < rows)
+      *reinterpret_cast<u32x4_t*>(dst + static_cast<size_t>(row) * ld + col0 + cs * 8) =
+          *reinterpret_cast<const u32x4_t*>(lds + row * pitch + cs * 16);
+  }
+}
+
 // gate/up + SwiGLU, KSPLIT = 1: each wave owns MB 16-row blocks of gate and
 // of up (64 MB rows per workgroup) over the full K = H.  1-D grid over
 // (tile, slice) items, block 256.
@@ -625,15 +659,17 @@ __device__ __forceinline__ void gateup_x_body(
     uint16_t* __restrict__ h, char (*xs)[NB * 4096]) {
   // wave index as a uniform value (the slab base below must live in SGPRs)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int r = lane & 15, q = lane >> 4;
+  const int r = lane & 15;
   const Dq dq = dq_consts<WF>();
   const int i0 = (sl * 4 + wave) * 16 * MB;
   const int units = H / 128;
   const size_t nb0 = (static_cast<size_t>(tl.e) * I + i0) / 16;
   const Slab<WF> Sg(wg, sg, nb0, MB, H), Su(wu, su, nb0, MB, H);
 
-  XUnit<NB> xu;
-  xu.init(x, [&](int R) {
+  // token rows through a raw buffer: T * H < 2^31 elements (an ABI limit),
+  // so the byte offsets fit 32 bits
+  XUnitBuf<NB> xu;
+  xu.init(x, static_cast<uint32_t>(static_cast<size_t>(P / k) * H * 2), [&](int R) {
     int p = sorted_pair[tl.row0 + min(R, tl.rows - 1)];
     p = min(max(p, 0), P - 1);
     return static_cast<size_t>(p / k) * H;
@@ -716,19 +752,9 @@ __device__ __forceinline__ void gateup_x_body(
     }
   });
 
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int i = i0 + mb * 16 + r;
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rr = b * 16 + 4 * q + j;
-        if (rr < tl.rows)
-          h[static_cast<size_t>(tl.row0 + rr) * I + i] =
-              f32_to_bf16(silu(acc[mb][0][b][j]) * acc[mb][1][b][j]);
-      }
-  }
+  store_tile<NB, MB>(
+      xs[0], [&](int mb, int b, int j) { return silu(acc[mb][0][b][j]) * acc[mb][1][b][j]; },
+      tl.rows, h + static_cast<size_t>(tl.row0) * I, I, sl * 64 * MB);
 }
 
 template <int WF, int NB, int MB, bool ROLL>
@@ -758,7 +784,7 @@ __device__ __forceinline__ void down_x_body(const uint16_t* __restrict__ h,
                                             char (*xs)[NB * 4096]) {
   // wave index as a uniform value (the slab base below must live in SGPRs)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int r = lane & 15, q = lane >> 4;
+  const int r = lane & 15;
   const Dq dq = dq_consts<WF>();
   const int n0 = (sl * 4 + wave) * 16 * MB;
   const int units = I / 128;
@@ -821,17 +847,9 @@ __device__ __forceinline__ void down_x_body(const uint16_t* __restrict__ h,
       }
     }
   });
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int n = n0 + mb * 16 + r;
-#pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int rr = b * 16 + 4 * q + j;
-        if (rr < tl.rows) y[static_cast<size_t>(tl.row0 + rr) * H + n] = f32_to_bf16(acc[mb][b][j]);
-      }
-  }
+  store_tile<NB, MB>(
+      xs[0], [&](int mb, int b, int j) { return acc[mb][b][j]; }, tl.rows,
+      y + static_cast<size_t>(tl.row0) * H, H, sl * 64 * MB);
 }
 
 // float32 path (act and weights float32): one thread per output, float32

@@ -172,6 +172,39 @@ struct XUnit {
   }
 };
 
+// The same staging with the rows read through a raw buffer (base and size
+// in SGPRs, one 32-bit byte offset per row instead of a 64-bit pointer).
+// The matrix must be under 4 GiB; loads past its size return 0.
+template <int NB>
+struct XUnitBuf {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t src[NB];   // byte offset of the row base + chunk
+  int dst[NB];
+  u32x4_t v[NB];
+
+  template <typename RowOf>
+  __device__ __forceinline__ void init(const uint16_t* base, uint32_t bytes, RowOf row_of) {
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, static_cast<int>(bytes),
+                                           0x00020000);
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int c = l & 15, r = 4 * w + (l >> 4);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      src[i] = static_cast<uint32_t>((row_of(16 * i + r) + c * 8) * 2);
+      dst[i] = (((c >> 2) * NB + i) * 64 + 16 * (c & 3) + (r ^ c)) * 16;
+    }
+  }
+  __device__ __forceinline__ void load(int u) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      v[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(src[i]), 256 * u, 0);
+  }
+  __device__ __forceinline__ void store(char* buf) const {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) *reinterpret_cast<u32x4_t*>(buf + dst[i]) = v[i];
+  }
+};
+
 // A fragment (k chunk st, row block b) of the staged unit in `buf`.
 template <int NB>
 __device__ __forceinline__ u32x4_t xfrag(const char* buf, int st, int b, int lane) {

@@ -102,6 +102,44 @@ __device__ __forceinline__ bool single_tile(const int32_t* __restrict__ tiles, i
   return (ti == 0 || tiles[3 * (ti - 1)] != e) && (ti + 1 >= n || tiles[3 * (ti + 1)] != e);
 }
 
+// The bf16 output tile of a 256-thread item -- rows 0 .. 16 NB - 1 of the
+// tile, columns col0 .. col0 + 64 MB - 1 -- written through LDS: value(mb, b,
+// j) of lane (r, q) in wave w is row 16 b + 4 q + j, column 16 (MB w + mb) +
+// r, so direct stores would be 2-byte scatters (4 MB NB per lane); staged,
+// each thread stores 16 contiguous bytes.  `lds` holds out_tile_bytes<NB,
+// MB>() bytes that no wave still reads.
+template <int NB, int MB>
+constexpr int out_tile_bytes() {
+  return 16 * NB * (128 * MB + 16);
+}
+template <int NB, int MB, typename Val>
+__device__ __forceinline__ void store_tile(char* lds, Val&& val, int rows,
+                                           uint16_t* __restrict__ dst, size_t ld, int col0) {
+  constexpr int pitch = 128 * MB + 16;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, q = lane >> 4;
+  __syncthreads();   // every wave is done with the buffer
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint16_t*>(lds + (16 * b + 4 * q + j) * pitch +
+                                     (16 * (MB * wave + mb) + r) * 2) = f32_to_bf16(val(mb, b, j));
+  __syncthreads();
+  constexpr int segs = 8 * MB;          // 16-byte segments per row
+  constexpr int total = 16 * NB * segs;  // segments in the tile (128 at NB = MB = 1)
+#pragma unroll
+  for (int it = 0; it < (total + 255) / 256; ++it) {
+    const int g = it * 256 + static_cast<int>(threadIdx.x);
+    const int row = g / segs, cs = g % segs;
+    if (g < total && row < rows)
+      *reinterpret_cast<u32x4_t*>(dst + static_cast<size_t>(row) * ld + col0 + cs * 8) =
+          *reinterpret_cast<const u32x4_t*>(lds + row * pitch + cs * 16);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Tiled weights (MOE_F_TILED_WEIGHTS).  The unit of the k loop is 128 k = 4
 // MFMA chunks; for one 16-row block a lane fetches, per unit, 4 x 16 B (bf16:

@@ -293,14 +293,20 @@ def test_stack_teacher_forced_int2():
 # Properties and edge cases
 # --------------------------------------------------------------------------
 
-def test_determinism_three_runs():
-    case, _ = get("decode")
+@pytest.mark.parametrize("name,layout", [("decode", "row"), ("decode", "tiled"),
+                                         ("bf16_tiles128", "tiled"), ("int4_many_rows", "tiled"),
+                                         ("int2_small", "tiled")])
+def test_determinism_three_runs(name, layout):
+    """Bitwise-identical outputs, routes and permutation over three runs
+    (each kernel family: small tiles, 64-row low-bit tiles, 128-row tiles)."""
+    case, _ = get(name)
     cfg = case.cfg
+    tiled = layout == "tiled"
     outs = []
     for i in range(3):
-        buf = buffers(cfg)
-        say(f"[determinism] run {i}")
-        buf.layer(case.li.x, case.li.w_router, case.li.bias, case.ex_gpu)
+        buf = buffers(cfg, tiled)
+        say(f"[determinism {name} {layout}] run {i}")
+        buf.layer(case.li.x, case.li.w_router, case.li.bias, case.experts(tiled))
         sync()
         outs.append((buf.out.view(torch.int16).cpu().numpy(), buf.topk_ids.cpu().numpy(),
                      buf.topk_w.cpu().numpy(), buf.sorted_pair.cpu().numpy()))

@@ -561,13 +561,14 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
 // ---------------------------------------------------------------------------
 // Large batches: token rows staged through LDS.
 //
-// With 64-row token tiles every wave of a workgroup needs the same token
-// fragments; loading them per wave makes the per-CU load path (not HBM) the
-// limit.  Here the workgroup copies each 64 x 128 token unit into LDS once,
-// with full 256-byte row segments per load, already in MFMA fragment order,
-// and the waves read their A fragments from LDS; weights still stream from
-// HBM straight into registers.  Two LDS buffers: the next unit is loaded
-// into registers while the current one is multiplied, then stored.
+// With 64- or 128-row token tiles every wave of a workgroup needs the same
+// token fragments; loading them per wave makes the per-CU load path (not
+// HBM) the limit.  Here the workgroup copies each 16 NB x 128 token unit into
+// LDS once, with full 256-byte row segments per load, already in MFMA
+// fragment order, and the waves read their A fragments from LDS; weights
+// still stream from HBM straight into registers.  Two LDS buffers: the next
+// unit is loaded into registers while the current one is multiplied, then
+// stored.  After the k loop the same buffers stage the output tile.
 
 // The k loop of the LDS-staged kernels.  Unit u multiplies the weights in
 // registers with the token unit in LDS buffer u & 1, while the token unit
@@ -962,9 +963,9 @@ template <int WF, int NB>
 constexpr bool tile_pf() {
   return WF == WF_BF16 && NB == 1;
 }
-// LDS-staged kernels (64-row tiles): bf16 gate/up issues each weight
-// fragment group a unit ahead (staged_loop with ROLL).  Measured on the
-// MI355X: gate/up 800 -> 769 us at 4096 tokens and 2640 -> 2510 us at 32768;
+// LDS-staged kernels: bf16 gate/up issues each weight fragment group a unit
+// ahead (staged_loop with ROLL).  Measured on the MI355X at 64-row tiles:
+// gate/up 800 -> 769 us at 4096 tokens and 2640 -> 2510 us at 32768;
 // down (5 k units) was 9 / 30 us slower with it, the low-bit formats have one
 // load per block and unit and nothing to roll.
 template <int WF, bool GATEUP>

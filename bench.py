@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -151,11 +152,24 @@ DIGEST_FILES = ("sparse_moe_routed_amd/csrc/k_ffn.hip", "sparse_moe_routed_amd/c
                 "sparse_moe_routed_amd/csrc/moe_internal.h", "sparse_moe_routed_amd/build.py")
 
 
+def _code_only(name, text):
+    """Source text without comments and with whitespace collapsed, so that
+    the digest changes with the code, not with its comments."""
+    if name.endswith(".py"):
+        text = re.sub(r"(?m)^\s*#.*$", "", text)
+    else:
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+    return " ".join(text.split())
+
+
 def kernel_source_digest():
+    """Digest of the FFN kernel sources (code only): the committed PMC
+    summaries count for the dominant kernel only while it matches."""
     h = hashlib.sha256()
     for f in DIGEST_FILES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(os.path.basename(f).encode() + fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(os.path.basename(f).encode() + _code_only(f, fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -515,12 +515,13 @@ def test_hot_experts_many_tiles():
     check_values(decode(buf.out, cfg.act), ref.out, cfg.act, "out")
 
 
-def test_max_experts():
-    cfg = C2.with_(T=40, H=256, E=1024, I=64, k=32)
+@pytest.mark.parametrize("T", [24, 40])   # 32-token permutation path and the general one
+def test_max_experts(T):
+    cfg = C2.with_(T=T, H=256, E=1024, I=64, k=32)
     case = make_case(cfg)
     ref = O.moe_layer(case.x64, case.wr64, None, case.ex_oracle, cfg.k)
     buf = buffers(cfg)
-    say("[E=1024, k=32]")
+    say(f"[E=1024, k=32, T={T}]")
     buf.layer(case.li.x, case.li.w_router, None, case.ex_gpu)
     sync()
     _, same = check_routes(buf.topk_ids.cpu().numpy(), buf.topk_w.cpu().numpy().astype(np.float64),

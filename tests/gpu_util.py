@@ -133,3 +133,26 @@ def check_values(got64, ref64, act, what):
     else:
         assert mx <= TOL_BF16_ABS and rl2 <= TOL_BF16_RL2, f"{what}: max-abs {mx} rel-L2 {rl2}"
     return dict(max_abs=mx, rel_l2=rl2)
+
+
+def cxx_oracle_layer(case: Case):
+    """The layer through the C++ float64 oracle on the case's input bytes.
+
+    The host copies of the expert arrays are zero-filled (untouched pages
+    cost no memory) except the experts the routes select, which are copied
+    from the device; the numpy oracle's router names them."""
+    from oracle import oracle_c as C
+    cfg, ex = case.cfg, case.li.experts
+    need = np.unique(O.select_topk(O.router_logits(case.x64, case.wr64, case.bias64), cfg.k))
+    host = {}
+    for n, t in ex.items():
+        if t is None:
+            host[n] = None
+            continue
+        st = tensor_to_numpy_storage(t[:1])
+        a = np.zeros((t.shape[0],) + st.shape[1:], dtype=st.dtype)
+        for e in need:
+            a[int(e)] = tensor_to_numpy_storage(t[int(e)])
+        host[n] = a
+    res = case.x64 if cfg.residual else None
+    return C.moe_layer_c(case.x64, case.wr64, case.bias64, host, cfg.wfmt, cfg.act, cfg.k, res)

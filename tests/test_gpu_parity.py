@@ -183,6 +183,33 @@ def test_layer_end_to_end(name, layout):
     say(f"[case {name}] layer routes {stats} out {vs}")
 
 
+CXX_CASES = [("tiny", None), ("decode", None), ("bf16_ragged", None), ("int4_small", None),
+             ("int2_small", None), ("bf16_tiles128_ragged", None), ("verify_int2_layer0", C5)]
+
+
+@pytest.mark.parametrize("name,full", CXX_CASES, ids=[n for n, _ in CXX_CASES])
+def test_layer_against_cxx_oracle(name, full):
+    """The whole layer (row-major and, where it applies, tiled weights)
+    against the plain C++ float64 oracle: routes bit-exact except near ties,
+    every output element within the output tolerance."""
+    from tests.gpu_util import cxx_oracle_layer
+    case = make_case(full) if full is not None else get(name)[0]
+    cfg = case.cfg
+    say(f"[cxx {name}] C++ oracle: {cfg}")
+    ref = cxx_oracle_layer(case)
+    res = case.li.x if cfg.residual else None
+    for tiled in (False, True) if tiled_ok(cfg) else (False,):
+        buf = buffers(cfg, tiled)
+        say(f"[cxx {name} tiled={tiled}] moe_layer")
+        buf.layer(case.li.x, case.li.w_router, case.li.bias, case.experts(tiled), residual=res)
+        sync()
+        stats, same = check_routes(buf.topk_ids.cpu().numpy(),
+                                   buf.topk_w.cpu().numpy().astype(np.float64),
+                                   ref.logits, ref.ids, ref.w, cfg.k)
+        vs = check_values(decode(buf.out, cfg.act)[same], ref.out[same], cfg.act, "out")
+        say(f"[cxx {name} tiled={tiled}] routes {stats} out {vs}")
+
+
 # --------------------------------------------------------------------------
 # Full-size workloads (sampled where the oracle cannot do every output)
 # --------------------------------------------------------------------------

@@ -106,6 +106,31 @@ def test_permute(name):
     assert np.array_equal(act[:p.n_active], p.active) and (act[p.n_active:] == -1).all()
 
 
+# Seeded random routes (distinct experts per token) across the permutation
+# paths: 32-token kernel, one workgroup (bitmap + prefixes up to 48 KB of
+# LDS), chunked (beyond it); the boundary shapes on both sides of each.
+PERM_RANDOM = [(1, 10, 512), (32, 10, 512), (33, 10, 512), (384, 10, 512), (385, 10, 512),
+               (1025, 10, 512), (2000, 10, 512), (192, 8, 1024), (193, 8, 1024), (700, 1, 16)]
+
+
+@pytest.mark.parametrize("T,k,E", PERM_RANDOM)
+def test_permute_random_routes(T, k, E):
+    rng = np.random.default_rng(2000 + T + k + E)
+    ids = np.array([rng.choice(E, size=k, replace=False) for _ in range(T)], dtype=np.int64)
+    p = O.permutation(ids, E)
+    buf = M.MoELayerBuffers(T, 128, E, 64, k, "bf16", "dense", device=DEV)
+    say(f"[permute random T={T} k={k} E={E}]")
+    buf.permute(topk_ids=i32(ids))
+    sync()
+    assert np.array_equal(buf.counts.cpu().numpy(), p.counts)
+    assert np.array_equal(buf.offsets.cpu().numpy(), p.offsets)
+    assert np.array_equal(buf.sorted_pair.cpu().numpy(), p.sorted_pair)
+    assert np.array_equal(buf.pair_row.cpu().numpy(), p.pair_row)
+    assert int(buf.n_active.item()) == p.n_active
+    act = buf.active.cpu().numpy()
+    assert np.array_equal(act[:p.n_active], p.active) and (act[p.n_active:] == -1).all()
+
+
 def _oracle_perm_tensors(p):
     t = [i32(p.counts), i32(p.offsets), i32(p.sorted_pair), i32(p.pair_row),
          i32(np.concatenate([p.active, -np.ones(len(p.counts) - p.n_active)])), i32([p.n_active])]

@@ -460,7 +460,11 @@ __global__ __launch_bounds__(256) void k_gateup_t(
 
 // down on tiled weights: MB 16-row blocks of output features per wave,
 // 64 MB per workgroup, full K = I.  1-D grid over (tile, slice) items, block 256.
-template <int WF, int NB, int MB, bool PF>
+// SH: the tile's intermediate rows [16 NB][I] are copied into LDS once (rows
+// of 2 I + 16 bytes, dynamic LDS) and the four waves read their fragments
+// there, instead of each wave gathering the same rows from L2 for every k
+// unit.
+template <int WF, int NB, int MB, bool PF, bool SH>
 __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
                                                 const uint8_t* __restrict__ wd,
                                                 const uint16_t* __restrict__ sd,
@@ -472,10 +476,36 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
   // faster
   constexpr bool kStageOut = MB >= 2;
   __shared__ __align__(16) char ot[kStageOut ? out_tile_bytes<NB, MB>() : 16];
+  extern __shared__ __align__(16) char hs[];   // SH: the intermediate rows
   int ti, sl;
   if (!tile_item(tiles[3 * max_tiles], H / (64 * MB), band, xcd != 0, ti, sl)) return;
   const Tile tl = read_tile(tiles, ti);
   if (tl.rows <= 0) return;
+  const int hp = 2 * I + 16;   // SH: LDS row pitch in bytes (rows 16 bytes = 4 banks apart)
+  if constexpr (SH) {
+    // 16-byte chunks; rows past the tile repeat its last row (never stored)
+    const int cpr = I / 8, nch = 16 * NB * cpr;
+    for (int c0 = threadIdx.x; c0 < nch; c0 += 4 * 256) {
+      u32x4_t v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = c0 + i * 256;
+        if (c < nch) {
+          const int row = c / cpr, c8 = c - row * cpr;
+          v[i] = ld16(h + static_cast<size_t>(tl.row0 + min(row, tl.rows - 1)) * I + c8 * 8);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = c0 + i * 256;
+        if (c < nch) {
+          const int row = c / cpr, c8 = c - row * cpr;
+          *reinterpret_cast<u32x4_t*>(hs + row * hp + c8 * 16) = v[i];
+        }
+      }
+    }
+    __syncthreads();
+  }
   // wave index as a uniform value (the slab base below must live in SGPRs)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
@@ -497,7 +527,8 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
   struct Stage {
     Scales<4> sc[MB];
     TRaw<WF> raw[MB];
-    u32x4_t ha[4][NB];
+    u32x4_t ha[SH ? 1 : 4][NB];
+    int u;
   };
   auto load = [&](Stage& S, int u) {
     if constexpr (WF != WF_BF16) {
@@ -506,31 +537,44 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) S.raw[mb] = tload<WF, weight_aux<NB>()>(Sd, mb, u, lane);
+    if constexpr (!SH) {
 #pragma unroll
-    for (int st = 0; st < 4; ++st)
+      for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) S.ha[st][b] = ld16(ph[b] + 128 * u + 32 * st);
+        for (int b = 0; b < NB; ++b) S.ha[st][b] = ld16(ph[b] + 128 * u + 32 * st);
+    }
+    S.u = u;
+  };
+  auto hfrag = [&](const Stage& S, int st, int b) -> u32x4_t {
+    if constexpr (SH)
+      return *reinterpret_cast<const u32x4_t*>(hs + (b * 16 + r) * hp +
+                                               (128 * S.u + 32 * st + 8 * q) * 2);
+    else
+      return S.ha[st][b];
   };
   auto compute = [&](const Stage& S) {
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
+      u32x4_t ha[NB];
+#pragma unroll
+      for (int b = 0; b < NB; ++b) ha[b] = hfrag(S, st, b);
       f32x4_t corr[NB];
       if constexpr (WF != WF_BF16) {
 #pragma unroll
         for (int b = 0; b < NB; ++b)
-          corr[b] = mfma_bf16(S.ha[st][b], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+          corr[b] = mfma_bf16(ha[b], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const u32x4_t wv = tdecode<WF>(S.raw[mb], st, dq);
         if constexpr (WF == WF_BF16) {
 #pragma unroll
-          for (int b = 0; b < NB; ++b) acc[mb][b] = mfma_bf16(S.ha[st][b], wv, acc[mb][b]);
+          for (int b = 0; b < NB; ++b) acc[mb][b] = mfma_bf16(ha[b], wv, acc[mb][b]);
         } else {
           const float sv = fp16_to_f32(S.sc[mb].s[st]);
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
-            const f32x4_t pp = mfma_bf16(S.ha[st][b], wv, corr[b]);
+            const f32x4_t pp = mfma_bf16(ha[b], wv, corr[b]);
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[mb][b][j] = fmaf(sv, pp[j], acc[mb][b][j]);
           }
@@ -1093,10 +1137,15 @@ static void down_tiled_launch(const moe_shape& s, const Plan& pl, const void* h,
                        ex.down_scale, tiles, pl.max_tiles, s.H, s.I, static_cast<uint16_t*>(y),
                        min(o.band, pl.max_tiles * split), o.xcd, split);
   } else {
-    hipLaunchKernelGGL((k_down_t<WF, NB, MB, tile_pf<WF, NB>()>), item_grid(pl, s.H / (64 * MB)),
-                       dim3(256), 0, st, static_cast<const uint16_t*>(h),
-                       static_cast<const uint8_t*>(ex.down), ex.down_scale, tiles, pl.max_tiles,
-                       s.H, s.I, static_cast<uint16_t*>(y), min(o.band, pl.max_tiles), o.xcd);
+    // low-bit single-block tiles stage their intermediate rows in LDS
+    const size_t lds = static_cast<size_t>(16 * NB) * (2 * s.I + 16);
+    const bool sh = WF != WF_BF16 && NB == 1 && lds <= 64 * 1024;
+    auto kern = sh ? k_down_t<WF, NB, MB, tile_pf<WF, NB>(), true>
+                   : k_down_t<WF, NB, MB, tile_pf<WF, NB>(), false>;
+    hipLaunchKernelGGL(kern, item_grid(pl, s.H / (64 * MB)), dim3(256), sh ? lds : 0, st,
+                       static_cast<const uint16_t*>(h), static_cast<const uint8_t*>(ex.down),
+                       ex.down_scale, tiles, pl.max_tiles, s.H, s.I, static_cast<uint16_t*>(y),
+                       min(o.band, pl.max_tiles), o.xcd);
   }
 }
 

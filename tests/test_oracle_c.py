@@ -64,6 +64,9 @@ def test_c_oracle_matches_numpy_oracle(name):
     ref = O.moe_layer(x64, wr64, b64, ex, cfg.k, residual=res)
     _close(got.logits, ref.logits, "logits")
     np.testing.assert_array_equal(got.ids, ref.ids)
+    # the rank-count selection equals a stable sort on (-logit, index)
+    order = np.argsort(-got.logits, axis=1, kind="stable")[:, :cfg.k]
+    np.testing.assert_array_equal(got.ids, order)
     _close(got.w, ref.w, "weights")
     np.testing.assert_array_equal(got.perm.counts, ref.perm.counts)
     np.testing.assert_array_equal(got.perm.offsets, ref.perm.offsets)

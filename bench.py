@@ -384,10 +384,11 @@ def main():
     fw = None if (args.no_fused or not tiled or T * k > 16384) else fused_waves(M, torch, dev, cfg, layers, xs)
 
     # ---- CPU oracle on a bounded sample --------------------------------------
-    cpu = None
+    cpu = cpu_cxx = None
     if not args.no_cpu_baseline:
         del buf
         cpu = cpu_baseline(cfg, L, layers, xs, args.cpu_seconds, dev)
+        cpu_cxx = cpu_baseline_cxx(cfg, L, layers, xs, args.cpu_seconds, dev)
 
     line = {
         "metric": "routed-MoE layer tokens/s",
@@ -438,6 +439,7 @@ def main():
         "offload": off,
         "fused_waves": fw,
         "cpu_baseline": cpu,
+        "cpu_baseline_cxx": cpu_cxx,
         "host_wall_s": round(wall, 3),
     }
     print(json.dumps(line))
@@ -727,6 +729,62 @@ def cpu_baseline(cfg, L, layers, xs, budget_s, dev):
                       f"{'' if tcpu == cfg.T else ' of the ' + str(cfg.T)} tokens (float64 numpy oracle, "
                       f"{'extrapolated to ' + str(L) + ' layers' if L > 1 else 'whole layer'}); "
                       f"host copies of the selected experts excluded"}
+
+
+def cpu_baseline_cxx(cfg, L, layers, xs, budget_s, dev):
+    """The plain C++ float64 oracle (oracle/moe_oracle_c.cpp), untuned, on a
+    bounded sample: the first min(T, 64) tokens of each batch through the
+    first layer(s) until the budget is spent, extrapolated per layer like
+    cpu_baseline.  Its inputs are host copies of the batch and of the experts
+    the sample selects (the others stay zero pages); copies are not timed.
+    One thread per output row, all host cores."""
+    import torch
+
+    from moe_inputs import make_experts
+    from moe_inputs import tensor_to_numpy_storage as npy
+    from oracle import moe_oracle as O
+    from oracle import oracle_c as C
+
+    threads = os.cpu_count() or 1
+    tcpu = min(cfg.T, 64)
+    layer_s = []
+    t_budget = time.perf_counter()
+    for b in range(len(xs)):
+        x64 = O.decode_act(npy(xs[b][:tcpu]), cfg.act)
+        for l in range(L):
+            wr, bias, _, _ = layers[l]
+            ex = make_experts(cfg, l, dev)
+            wr64 = O.decode_act(npy(wr), cfg.act)
+            b64 = None if bias is None else bias.double().cpu().numpy()
+            need = np.unique(O.select_topk(O.router_logits(x64, wr64, b64), cfg.k))
+            host = {}
+            for n, t in ex.items():
+                if t is None:
+                    host[n] = None
+                    continue
+                one = npy(t[:1])
+                a = np.zeros((t.shape[0],) + one.shape[1:], dtype=one.dtype)
+                for e in need:
+                    a[int(e)] = npy(t[int(e)])
+                host[n] = a
+            del ex
+            torch.cuda.empty_cache()
+            t0 = time.perf_counter()
+            r = C.moe_layer_c(x64, wr64, b64, host, cfg.wfmt, cfg.act, cfg.k,
+                              x64 if cfg.residual else None, threads=threads)
+            layer_s.append(time.perf_counter() - t0)
+            x64 = O.act_round(r.out, cfg.act)
+            if time.perf_counter() - t_budget > budget_s:
+                break
+        if time.perf_counter() - t_budget > budget_s:
+            break
+    per_layer = sum(layer_s) / len(layer_s)
+    return {"value": round(tcpu / (per_layer * L), 3), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(layer_s)} layer passes of {tcpu}"
+                      f"{'' if tcpu == cfg.T else ' of the ' + str(cfg.T)} tokens (float64 C++ oracle, "
+                      f"{'extrapolated to ' + str(L) + ' layers' if L > 1 else 'whole layer'}); "
+                      f"host copies excluded"}
 
 
 if __name__ == "__main__":

@@ -10,8 +10,8 @@ as it does between decode batches.
 
 Prints one JSON line: tokens/s of the workload, the roofline of the dominant
 kernel (the grouped gate/up + SwiGLU kernel, timed with HIP events around
-each of its launches on the stream it runs on), and the CPU oracle timed on a
-bounded sample of the same workload.
+each of its launches on the stream it runs on), and the two CPU oracles
+(float64 numpy, float64 C++) timed on bounded samples of the same workload.
 """
 from __future__ import annotations
 

@@ -196,7 +196,7 @@ def traffic_from_profiles(workload, digest):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
 

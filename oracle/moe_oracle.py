@@ -1,7 +1,7 @@
 """Plain CPU oracle for the routed sparse-MoE layer (TEST INFRASTRUCTURE ONLY).
 
 This module is the executable specification the HIP path is checked against.
-Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline legs of
 ``bench.py`` may import it; the product library never does, and it shares no
 code, table or helper with the HIP path.  Everything is computed in float64
 from the exact stored input values (bf16, fp16, fp32 and small integers all

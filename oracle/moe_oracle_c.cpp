@@ -1,7 +1,7 @@
 // Plain, slow CPU oracle of the routed sparse-MoE layer in C++ (TEST
 // INFRASTRUCTURE ONLY).
 //
-// Only tests/, __graft_entry__.smoke() and the cpu_baseline leg of bench.py
+// Only tests/, __graft_entry__.smoke() and the CPU-baseline legs of bench.py
 // may load it; the product library never does, and it shares no code, table
 // or helper with the HIP path (nor with the numpy oracle beside it, which it
 // is checked against).  Everything is float64 on the exact stored values:

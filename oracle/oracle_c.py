@@ -1,5 +1,6 @@
 """ctypes binding of the C++ oracle ``moe_oracle_c.cpp`` (TEST INFRASTRUCTURE
-ONLY: loaded by ``tests/`` and nothing in the product path).
+ONLY: loaded by ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
+legs of ``bench.py``; nothing in the product path).
 
 The C++ oracle is a second, independently written plain CPU implementation
 of the routed layer in float64; ``tests/test_oracle_c.py`` checks it against

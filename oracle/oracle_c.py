@@ -101,6 +101,37 @@ def storage_arrays(experts: dict) -> dict:
     return out
 
 
+def routes_c(x64: np.ndarray, wr64: np.ndarray, bias64: Optional[np.ndarray], k: int,
+             threads: Optional[int] = None):
+    """Router logits, top-k ids, weights and the permutation through the C++
+    oracle (no expert FFN): (logits, ids, w, PermC)."""
+    lib = load()
+    x64 = np.ascontiguousarray(x64, dtype=np.float64)
+    wr64 = np.ascontiguousarray(wr64, dtype=np.float64)
+    b64 = None if bias64 is None else np.ascontiguousarray(bias64, dtype=np.float64)
+    T, H = x64.shape
+    E = wr64.shape[0]
+    th = threads or min(16, os.cpu_count() or 1)
+    logits = np.empty((T, E))
+    lib.oc_router_logits(T, H, E, _p(x64), _p(wr64), _p(b64), th, _p(logits))
+    ids = np.empty((T, k), dtype=np.int32)
+    if lib.oc_select_topk(T, E, k, _p(logits), th, _p(ids)) != 0:
+        raise ValueError("non-finite router logits")
+    w = np.empty((T, k))
+    lib.oc_route_weights(T, E, k, _p(logits), _p(ids), _p(w))
+    P = T * k
+    counts = np.empty(E, dtype=np.int32)
+    offsets = np.empty(E + 1, dtype=np.int32)
+    sp = np.empty(P, dtype=np.int32)
+    pr = np.empty(P, dtype=np.int32)
+    active = np.empty(E, dtype=np.int32)
+    n_act = lib.oc_permutation(P, E, _p(ids), _p(counts), _p(offsets), _p(sp), _p(pr),
+                               _p(active))
+    perm = PermC(counts.astype(np.int64), offsets.astype(np.int64), sp.astype(np.int64),
+                 pr.astype(np.int64), active[:n_act].astype(np.int64), int(n_act))
+    return logits, ids.astype(np.int64), w, perm
+
+
 def moe_layer_c(x64: np.ndarray, wr64: np.ndarray, bias64: Optional[np.ndarray], experts: dict,
                 wfmt: str, act: str, k: int, residual64: Optional[np.ndarray] = None,
                 threads: Optional[int] = None) -> LayerC:

@@ -235,6 +235,32 @@ def test_layer_against_cxx_oracle(name, full):
         say(f"[cxx {name} tiled={tiled}] routes {stats} out {vs}")
 
 
+def test_full_prefill_routes_against_cxx_oracle():
+    """Full-size prefill (4096 tokens, Zipf bias): routes and the permutation
+    of the HIP path against the C++ oracle's, bit-exact except near ties
+    (moe_permute is fed the oracle's ids, so the permutation is compared
+    exactly)."""
+    from oracle import oracle_c as C
+    cfg = C3
+    case = make_case(cfg)
+    say("[cxx prefill routes] C++ oracle routes")
+    logits, ids, w, perm = C.routes_c(case.x64, case.wr64, case.bias64, cfg.k)
+    buf = buffers(cfg)
+    say("[cxx prefill routes] moe_route")
+    buf.route(case.li.x, case.li.w_router, case.li.bias)
+    sync()
+    stats, _ = check_routes(buf.topk_ids.cpu().numpy(), buf.topk_w.cpu().numpy().astype(np.float64),
+                            logits, ids, w, cfg.k)
+    say(f"[cxx prefill routes] {stats}; moe_permute on the C++ oracle's ids")
+    buf.permute(topk_ids=i32(ids))
+    sync()
+    assert np.array_equal(buf.counts.cpu().numpy(), perm.counts)
+    assert np.array_equal(buf.offsets.cpu().numpy(), perm.offsets)
+    assert np.array_equal(buf.sorted_pair.cpu().numpy(), perm.sorted_pair)
+    assert np.array_equal(buf.pair_row.cpu().numpy(), perm.pair_row)
+    assert int(buf.n_active.item()) == perm.n_active
+
+
 # --------------------------------------------------------------------------
 # Full-size workloads (sampled where the oracle cannot do every output)
 # --------------------------------------------------------------------------

@@ -110,6 +110,18 @@ def test_c_oracle_k_equals_E_keeps_all_experts_in_logit_order():
     np.testing.assert_array_equal(got.perm.counts, np.full(cfg.E, cfg.T))
 
 
+def test_c_oracle_routes_only_equals_layer():
+    cfg = CASES["bf16_zipf"]
+    x64, wr64, b64, st, _, _ = _inputs(cfg)
+    full = C.moe_layer_c(x64, wr64, b64, st, cfg.wfmt, cfg.act, cfg.k)
+    logits, ids, w, perm = C.routes_c(x64, wr64, b64, cfg.k)
+    np.testing.assert_array_equal(logits, full.logits)
+    np.testing.assert_array_equal(ids, full.ids)
+    np.testing.assert_array_equal(w, full.w)
+    for f in ("counts", "offsets", "sorted_pair", "pair_row", "active"):
+        np.testing.assert_array_equal(getattr(perm, f), getattr(full.perm, f))
+
+
 def test_c_oracle_thread_count_is_bit_invariant():
     cfg = CASES["int4_residual"]
     x64, wr64, b64, st, _, res = _inputs(cfg)

@@ -135,15 +135,19 @@ def check_values(got64, ref64, act, what):
     return dict(max_abs=mx, rel_l2=rl2)
 
 
-def cxx_oracle_layer(case: Case):
-    """The layer through the C++ float64 oracle on the case's input bytes.
+def cxx_oracle_layer(case: Case, tokens=None):
+    """The layer through the C++ float64 oracle on the case's input bytes,
+    for all tokens or for the rows `tokens` (every step is per token except
+    the row order of the permutation, so a subset gives those tokens' exact
+    outputs).
 
     The host copies of the expert arrays are zero-filled (untouched pages
     cost no memory) except the experts the routes select, which are copied
     from the device; the numpy oracle's router names them."""
     from oracle import oracle_c as C
     cfg, ex = case.cfg, case.li.experts
-    need = np.unique(O.select_topk(O.router_logits(case.x64, case.wr64, case.bias64), cfg.k))
+    x64 = case.x64 if tokens is None else case.x64[np.asarray(tokens)]
+    need = np.unique(O.select_topk(O.router_logits(x64, case.wr64, case.bias64), cfg.k))
     host = {}
     for n, t in ex.items():
         if t is None:
@@ -154,5 +158,5 @@ def cxx_oracle_layer(case: Case):
         for e in need:
             a[int(e)] = tensor_to_numpy_storage(t[int(e)])
         host[n] = a
-    res = case.x64 if cfg.residual else None
-    return C.moe_layer_c(case.x64, case.wr64, case.bias64, host, cfg.wfmt, cfg.act, cfg.k, res)
+    res = x64 if cfg.residual else None
+    return C.moe_layer_c(x64, case.wr64, case.bias64, host, cfg.wfmt, cfg.act, cfg.k, res)

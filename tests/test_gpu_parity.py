@@ -235,6 +235,29 @@ def test_layer_against_cxx_oracle(name, full):
         say(f"[cxx {name} tiled={tiled}] routes {stats} out {vs}")
 
 
+@pytest.mark.parametrize("name,cfg,layer", [("prefill", C3, 0), ("stack_int4", C4, 0),
+                                            ("stack_int4", C4, 47)])
+def test_full_layer_sampled_against_cxx_oracle(name, cfg, layer):
+    """One full-size layer (tiled weights) through moe_layer; 32 sampled
+    tokens through the C++ oracle; routes bit-exact except near ties and
+    those tokens' outputs within the bf16 tolerance."""
+    from tests.gpu_util import cxx_oracle_layer
+    case = make_case(cfg, layer=layer)
+    sample = np.sort(np.random.default_rng(77 + layer).choice(cfg.T, size=32, replace=False))
+    say(f"[cxx full {name} layer {layer}] C++ oracle on 32 tokens")
+    ref = cxx_oracle_layer(case, sample)
+    buf = buffers(cfg, tiled_ok(cfg))
+    res = case.li.x if cfg.residual else None
+    say(f"[cxx full {name} layer {layer}] moe_layer")
+    buf.layer(case.li.x, case.li.w_router, case.li.bias, case.experts(tiled_ok(cfg)), residual=res)
+    sync()
+    stats, same = check_routes(buf.topk_ids.cpu().numpy()[sample],
+                               buf.topk_w.cpu().numpy().astype(np.float64)[sample],
+                               ref.logits, ref.ids, ref.w, cfg.k)
+    vs = check_values(decode(buf.out, cfg.act)[sample][same], ref.out[same], cfg.act, "out")
+    say(f"[cxx full {name} layer {layer}] routes {stats} out {vs}")
+
+
 def test_full_prefill_routes_against_cxx_oracle():
     """Full-size prefill (4096 tokens, Zipf bias): routes and the permutation
     of the HIP path against the C++ oracle's, bit-exact except near ties

@@ -47,7 +47,9 @@
  *   H > 0 with H % 128 == 0, I > 0 with I % 32 == 0, H, I <= 65536,
  *   T * top_k < 2^31, T * max(E, H) < 2^31, and the FFN tile count bound
  *   T*top_k/(16*nb) + min(E, T*top_k) <= 65535 (nb = 1 for T <= 16, float32
- *   or T*top_k <= 12*E; else 2 for T <= 1024, else 4).
+ *   or T*top_k <= 12*E; else 2 for T <= 1024; else 8 for bf16 dense weights
+ *   in the tiled layout without MOE_F_FUSED_FFN once T*top_k >= 48*E and
+ *   I % 128 == 0; else 4).
  * Formats (MOE_E_DTYPE / MOE_E_FORMAT otherwise):
  *   act MOE_DT_F32  with wfmt MOE_WF_DENSE (float32 weights);
  *   act MOE_DT_BF16 with wfmt MOE_WF_DENSE (bf16 weights), MOE_WF_INT4_G32

@@ -159,9 +159,12 @@ void oc_route_weights(int T, int E, int k, const double* logits, const int32_t* 
 // Stable counting sort of the pairs p = t*k + j by expert ([P-019] "Why
 // overlap alone cannot defeat the byte roofline": rows grouped by expert):
 // counts, offsets (exclusive scan), row -> pair, pair -> row, the active
-// experts ascending.  Returns the number of active experts.
+// experts ascending.  Returns the number of active experts, or -1 (nothing
+// written) if an id is outside [0, E).
 int oc_permutation(int P, int E, const int32_t* ids, int32_t* counts, int32_t* offsets,
                    int32_t* sorted_pair, int32_t* pair_row, int32_t* active) {
+  for (int p = 0; p < P; ++p)
+    if (ids[p] < 0 || ids[p] >= E) return -1;
   for (int e = 0; e < E; ++e) counts[e] = 0;
   for (int p = 0; p < P; ++p) counts[ids[p]] += 1;
   offsets[0] = 0;

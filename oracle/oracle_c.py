@@ -127,6 +127,8 @@ def routes_c(x64: np.ndarray, wr64: np.ndarray, bias64: Optional[np.ndarray], k:
     active = np.empty(E, dtype=np.int32)
     n_act = lib.oc_permutation(P, E, _p(ids), _p(counts), _p(offsets), _p(sp), _p(pr),
                                _p(active))
+    if n_act < 0:
+        raise ValueError("expert id outside [0, E)")
     perm = PermC(counts.astype(np.int64), offsets.astype(np.int64), sp.astype(np.int64),
                  pr.astype(np.int64), active[:n_act].astype(np.int64), int(n_act))
     return logits, ids.astype(np.int64), w, perm
@@ -161,6 +163,8 @@ def moe_layer_c(x64: np.ndarray, wr64: np.ndarray, bias64: Optional[np.ndarray],
     active = np.empty(E, dtype=np.int32)
     n_act = lib.oc_permutation(P, E, _p(ids), _p(counts), _p(offsets), _p(sp), _p(pr),
                                _p(active))
+    if n_act < 0:
+        raise ValueError("expert id outside [0, E)")
     g, u, d = (np.ascontiguousarray(experts[n]) for n in ("gate", "up", "down"))
     gs, us, ds = (None if experts[n] is None else np.ascontiguousarray(experts[n])
                   for n in ("gate_scale", "up_scale", "down_scale"))

@@ -6,7 +6,9 @@ every expert, gated by the top-k mask), which shares no permutation or
 grouping with either: routes and the permutation bit-exact, float values to
 float64 summation-order noise.  Special cases that the pages fix are checked
 directly: equal logits go to the lower expert index, k = E keeps every
-expert, and the thread count does not change a bit of the result.
+expert, and the thread count does not change a bit of the result.  The
+low-bit decoders are pinned by closed forms: the most negative code (-8,
+-2) decodes as q * s, and codes sit lowest bits first within a byte.
 """
 import numpy as np
 import pytest
@@ -138,3 +140,53 @@ def test_c_oracle_rejects_non_finite_logits():
     x64[3, 7] = np.inf
     with pytest.raises(ValueError):
         C.moe_layer_c(x64, wr64, b64, st, cfg.wfmt, cfg.act, cfg.k)
+
+
+@pytest.mark.parametrize("wfmt,neg_byte,one_byte,qneg", [("int4_g32", 0x88, 0x11, -8),
+                                                         ("int2_g32", 0xAA, 0x55, -2)])
+def test_c_oracle_most_negative_code_closed_form(wfmt, neg_byte, one_byte, qneg):
+    # every gate code is the most negative one (never produced by the
+    # quantizer, still decoded as q * s), every up code +1, every down code
+    # the most negative one at scale 0.5: g = qneg S, u = S with S = sum(x),
+    # y_n = I * (0.5 qneg) * silu(g) * u
+    T, H, I, E = 1, 128, 32, 1
+    bits = 4 if wfmt == "int4_g32" else 2
+    rng = np.random.default_rng(5)
+    x = np.round(rng.standard_normal((T, H)) * 8) / 64        # exact in bf16
+    wr = np.zeros((E, H))
+    one, half = 0x3C00, 0x3800                                 # fp16 1.0, 0.5
+    st = {"gate": np.full((E, I, H * bits // 8), neg_byte, np.uint8),
+          "up": np.full((E, I, H * bits // 8), one_byte, np.uint8),
+          "down": np.full((E, H, I * bits // 8), neg_byte, np.uint8),
+          "gate_scale": np.full((E, I, H // 32), one, np.uint16),
+          "up_scale": np.full((E, I, H // 32), one, np.uint16),
+          "down_scale": np.full((E, H, I // 32), half, np.uint16)}
+    got = C.moe_layer_c(x, wr, None, st, wfmt, "bf16", 1)
+    S = x.sum()
+    g = qneg * S
+    a = g / (1.0 + np.exp(-g)) * S
+    np.testing.assert_allclose(got.out, np.full((T, H), I * 0.5 * qneg * a), rtol=1e-12)
+
+
+@pytest.mark.parametrize("wfmt,byte,codes", [("int4_g32", 0x1F, [-1, 1]),
+                                             ("int2_g32", 0x1B, [-1, -2, 1, 0])])
+def test_c_oracle_code_order_within_a_byte(wfmt, byte, codes):
+    # element c of a row sits at byte c*bits/8, bit (c*bits)%8, lowest first:
+    # with every byte equal, gate row i is the periodic pattern `codes`
+    T, H, I, E = 1, 128, 32, 1
+    bits = 4 if wfmt == "int4_g32" else 2
+    rng = np.random.default_rng(6)
+    x = np.round(rng.standard_normal((T, H)) * 8) / 64
+    one = 0x3C00
+    st = {"gate": np.full((E, I, H * bits // 8), byte, np.uint8),
+          "up": np.full((E, I, H * bits // 8), 0x11 if bits == 4 else 0x55, np.uint8),
+          "down": np.full((E, H, I * bits // 8), 0x11 if bits == 4 else 0x55, np.uint8),
+          "gate_scale": np.full((E, I, H // 32), one, np.uint16),
+          "up_scale": np.full((E, I, H // 32), one, np.uint16),
+          "down_scale": np.full((E, H, I // 32), one, np.uint16)}
+    got = C.moe_layer_c(x, np.zeros((E, H)), None, st, wfmt, "bf16", 1)
+    pattern = np.tile(np.array(codes, dtype=np.float64), H // len(codes))
+    g = float(pattern @ x[0])
+    S = x.sum()
+    a = g / (1.0 + np.exp(-g)) * S
+    np.testing.assert_allclose(got.out, np.full((T, H), I * a), rtol=1e-12)

@@ -258,6 +258,47 @@ def test_full_layer_sampled_against_cxx_oracle(name, cfg, layer):
     say(f"[cxx full {name} layer {layer}] routes {stats} out {vs}")
 
 
+@pytest.mark.parametrize("tiled", [False, True], ids=["row", "tiled"])
+@pytest.mark.parametrize("wfmt", ["int4_g32", "int2_g32"])
+def test_lowbit_full_code_range_against_cxx_oracle(wfmt, tiled):
+    """Uniformly random packed bytes, so every code occurs, including the
+    most negative one (-8, -2) that the quantizer never writes but that must
+    decode as q * s; random fp16 scales.  moe_layer against the C++ oracle."""
+    from oracle import oracle_c as C
+    T, H, E, I, k = 37, 256, 8, 128, 3
+    bits = 4 if wfmt == "int4_g32" else 2
+    rng = np.random.default_rng(11 + bits)
+    x = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(torch.bfloat16)
+    wr = torch.from_numpy((0.02 * rng.standard_normal((E, H))).astype(np.float32)).to(torch.bfloat16)
+    host = {}
+    for n, (rows, K) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        host[n] = rng.integers(0, 256, (E, rows, K * bits // 8), dtype=np.uint8)
+        host[n + "_scale"] = rng.uniform(0.002, 0.02, (E, rows, K // 32)).astype(np.float16)
+    dev = {n: torch.from_numpy(a).to(DEV) for n, a in host.items()}
+    ex = M.make_experts(dev["gate"], dev["up"], dev["down"], dev["gate_scale"], dev["up_scale"],
+                        dev["down_scale"])
+    keep = None
+    if tiled:
+        keep = {n: torch.empty_like(t) for n, t in dev.items()}
+        ext = M.make_experts(keep["gate"], keep["up"], keep["down"], keep["gate_scale"],
+                             keep["up_scale"], keep["down_scale"])
+        M.moe_tile_experts(M.make_shape(T, H, E, I, k, "bf16", wfmt), ex, ext)
+        ex = ext
+    buf = M.MoELayerBuffers(T, H, E, I, k, "bf16", wfmt, device=DEV, tiled=tiled)
+    xd, wrd = x.to(DEV), wr.to(DEV)
+    say(f"[full code range {wfmt} tiled={tiled}] moe_layer")
+    buf.layer(xd, wrd, None, ex)
+    sync()
+    st = {n: (a.view(np.uint16) if a.dtype == np.float16 else a) for n, a in host.items()}
+    x64, wr64 = x.double().numpy(), wr.double().numpy()
+    ref = C.moe_layer_c(x64, wr64, None, st, wfmt, "bf16", k)
+    stats, same = check_routes(buf.topk_ids.cpu().numpy(), buf.topk_w.cpu().numpy().astype(np.float64),
+                               ref.logits, ref.ids, ref.w, k)
+    vs = check_values(decode(buf.out, "bf16")[same], ref.out[same], "bf16", "out")
+    say(f"[full code range {wfmt} tiled={tiled}] routes {stats} out {vs}")
+    del keep
+
+
 def test_full_prefill_routes_against_cxx_oracle():
     """Full-size prefill (4096 tokens, Zipf bias): routes and the permutation
     of the HIP path against the C++ oracle's, bit-exact except near ties

@@ -40,23 +40,29 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def load_from(path: str):
+    """A library built from this source (or a copy of it) at `path`, with
+    its argument types declared."""
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i = ctypes.c_int
+    lib.oc_router_logits.argtypes = [i, i, i, P, P, P, i, P]
+    lib.oc_select_topk.argtypes = [i, i, i, P, i, P]
+    lib.oc_select_topk.restype = i
+    lib.oc_route_weights.argtypes = [i, i, i, P, P, P]
+    lib.oc_permutation.argtypes = [i, i, P, P, P, P, P, P]
+    lib.oc_permutation.restype = i
+    lib.oc_grouped_ffn.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, P, P, P, P, P, i, i, P]
+    lib.oc_combine.argtypes = [i, i, i, P, P, P, P, P]
+    return lib
+
+
 def load():
     global _lib
     if _lib is None:
         if not os.path.exists(LIB):
             build()
-        _lib = ctypes.CDLL(LIB)
-        P = ctypes.c_void_p
-        i = ctypes.c_int
-        _lib.oc_router_logits.argtypes = [i, i, i, P, P, P, i, P]
-        _lib.oc_select_topk.argtypes = [i, i, i, P, i, P]
-        _lib.oc_select_topk.restype = i
-        _lib.oc_route_weights.argtypes = [i, i, i, P, P, P]
-        _lib.oc_permutation.argtypes = [i, i, P, P, P, P, P, P]
-        _lib.oc_permutation.restype = i
-        _lib.oc_grouped_ffn.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, P, P, P, P, P, i, i,
-                                        P]
-        _lib.oc_combine.argtypes = [i, i, i, P, P, P, P, P]
+        _lib = load_from(LIB)
     return _lib
 
 
@@ -136,10 +142,11 @@ def routes_c(x64: np.ndarray, wr64: np.ndarray, bias64: Optional[np.ndarray], k:
 
 def moe_layer_c(x64: np.ndarray, wr64: np.ndarray, bias64: Optional[np.ndarray], experts: dict,
                 wfmt: str, act: str, k: int, residual64: Optional[np.ndarray] = None,
-                threads: Optional[int] = None) -> LayerC:
+                threads: Optional[int] = None, lib=None) -> LayerC:
     """The routed layer through the C++ oracle.  ``experts`` holds storage
-    arrays (``storage_arrays``): gate/up [E][I][H...], down [E][H][I...]."""
-    lib = load()
+    arrays (``storage_arrays``): gate/up [E][I][H...], down [E][H][I...].
+    ``lib``: another build of the source (load_from), else the default."""
+    lib = lib or load()
     x64 = np.ascontiguousarray(x64, dtype=np.float64)
     wr64 = np.ascontiguousarray(wr64, dtype=np.float64)
     b64 = None if bias64 is None else np.ascontiguousarray(bias64, dtype=np.float64)

@@ -115,8 +115,11 @@ def round_to_bf16(v: np.ndarray) -> np.ndarray:
     them as float64.  Used only at a stacked layer boundary (reading R7).
     Works on the significand directly so that there is exactly one rounding."""
     v = np.asarray(v, dtype=np.float64)
-    m, e = np.frexp(v)                      # v = m * 2**e, 0.5 <= |m| < 1
-    q = np.rint(np.ldexp(m, 8))             # bf16 keeps 8 significant bits
+    _, e = np.frexp(v)                      # v = m * 2**e, 0.5 <= |m| < 1
+    # bf16 keeps 8 significant bits in the binade 2**(e-1) .. 2**e; below
+    # 2**-126 its values are subnormal, on the fixed grid 2**-133
+    e = np.maximum(e, -125)
+    q = np.rint(np.ldexp(v, 8 - e))
     return np.ldexp(q, e - 8)
 
 

@@ -102,6 +102,41 @@ void decode_row(int wfmt, int act, const void* mat, const uint16_t* scales, int 
 
 extern "C" {
 
+// Activation storage -> double: act 0 float32 values, act 1 bf16 bit
+// patterns (exact in both cases).
+void oc_decode_act(int act, int64_t n, const void* src, double* dst) {
+  for (int64_t i = 0; i < n; ++i)
+    dst[i] = act == 0 ? static_cast<double>(static_cast<const float*>(src)[i])
+                      : bf16_to_double(static_cast<const uint16_t*>(src)[i]);
+}
+
+// double -> bf16 bit pattern, one rounding to nearest with ties to even (the
+// storage step between stacked layers: x_{l+1} is stored in the activation
+// type).  bf16 keeps 8 significant bits and float32's exponent range: the
+// value is rounded on the grid of its binade (ulp 2^(e-7) for 2^e <= |v| <
+// 2^(e+1), e >= -126; ulp 2^-133 below), then written through float32,
+// which holds every bf16 value exactly.  Finite inputs only; values that
+// round beyond the largest bf16 become infinity.
+void oc_round_bf16(int64_t n, const double* src, uint16_t* dst) {
+  for (int64_t i = 0; i < n; ++i) {
+    const double v = src[i];
+    double r = 0.0;
+    if (v != 0.0) {
+      int e = std::ilogb(v);
+      if (e < -126) e = -126;
+      const double q = std::nearbyint(std::ldexp(v, 7 - e));   // default mode: ties to even
+      r = std::ldexp(q, e - 7);
+    } else {
+      r = v;   // keeps the sign of zero
+    }
+    float f = static_cast<float>(r);   // exact unless it overflows
+    if (std::fabs(r) > 3.3895313892515355e38) f = r > 0 ? INFINITY : -INFINITY;
+    uint32_t u;
+    std::memcpy(&u, &f, sizeof u);
+    dst[i] = static_cast<uint16_t>(u >> 16);
+  }
+}
+
 // logits[t][e] = sum_{h ascending} x[t][h] * wr[e][h] (+ bias[e])
 // ([P-001] "Phase 1"; the bias is a reading of the pages).
 void oc_router_logits(int T, int H, int E, const double* x, const double* wr, const double* bias,

@@ -54,6 +54,8 @@ def load_from(path: str):
     lib.oc_permutation.restype = i
     lib.oc_grouped_ffn.argtypes = [i, i, i, i, i, i, i, P, P, P, P, P, P, P, P, P, P, i, i, P]
     lib.oc_combine.argtypes = [i, i, i, P, P, P, P, P]
+    lib.oc_decode_act.argtypes = [i, ctypes.c_int64, P, P]
+    lib.oc_round_bf16.argtypes = [ctypes.c_int64, P, P]
     return lib
 
 
@@ -104,6 +106,23 @@ def storage_arrays(experts: dict) -> dict:
             out[n] = t.view(torch.int16).numpy().view(np.uint16)
         else:
             out[n] = t.numpy()
+    return out
+
+
+def decode_act_c(storage: np.ndarray, act: str) -> np.ndarray:
+    """Activation storage (float32 values, or bf16 bit patterns as uint16)
+    decoded to float64 by the C++ oracle's own decoder."""
+    src = np.ascontiguousarray(storage, dtype=np.float32 if act == "f32" else np.uint16)
+    out = np.empty(src.shape, dtype=np.float64)
+    load().oc_decode_act(ACT[act], src.size, _p(src), _p(out))
+    return out
+
+
+def round_bf16_c(v64: np.ndarray) -> np.ndarray:
+    """float64 values rounded once to bf16 by the C++ oracle: bit patterns (uint16)."""
+    src = np.ascontiguousarray(v64, dtype=np.float64)
+    out = np.empty(src.shape, dtype=np.uint16)
+    load().oc_round_bf16(src.size, _p(src), _p(out))
     return out
 
 

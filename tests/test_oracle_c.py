@@ -190,3 +190,24 @@ def test_c_oracle_code_order_within_a_byte(wfmt, byte, codes):
     S = x.sum()
     a = g / (1.0 + np.exp(-g)) * S
     np.testing.assert_allclose(got.out, np.full((T, H), I * a), rtol=1e-12)
+
+
+def test_round_bf16_closed_forms_and_numpy():
+    """The C++ oracle's bf16 storage rounding: ties to even in the normal
+    and subnormal ranges, overflow to infinity, signed zero; and the same bits
+    as the numpy oracle over values spanning the whole exponent range."""
+    from oracle import moe_oracle as O
+    one = 1.0
+    cases = {one + 2**-8: 1.0, one + 3 * 2**-8: 1.0 + 2**-6, one + 2**-8 + 2**-30: 1.0 + 2**-7,
+             -(one + 3 * 2**-8): -(1.0 + 2**-6), 1.5 * 2.0**-133: 2.0**-132, 2.0**-134: 0.0,
+             2.0**-134 + 2.0**-160: 2.0**-133, 3.4e38: float("inf"), -3.4e38: float("-inf")}
+    v = np.array(list(cases))
+    got = C.decode_act_c(C.round_bf16_c(v), "bf16")
+    assert np.array_equal(got, np.array(list(cases.values())))
+    assert C.round_bf16_c(np.array([-0.0]))[0] == 0x8000
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal(50000) * np.exp(rng.uniform(-95, 95, 50000))
+    assert np.array_equal(C.round_bf16_c(w), O.bf16_bits_of(O.round_to_bf16(w)))
+    bits = rng.integers(0, 1 << 16, 4096).astype(np.uint16)
+    bits = bits[((bits >> 7) & 0xFF) != 0xFF]                  # finite patterns
+    assert np.array_equal(C.decode_act_c(bits, "bf16"), O.decode_bf16(bits))

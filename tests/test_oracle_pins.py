@@ -141,6 +141,11 @@ def test_round_to_bf16_ties_to_even():
     assert O.round_to_bf16(np.array([one + 3 * 2**-8]))[0] == 1.0 + 2**-6  # halfway -> even
     assert O.round_to_bf16(np.array([one + 2**-8 + 2**-30]))[0] == 1.0 + 2**-7
     assert O.round_to_bf16(np.array([-(one + 3 * 2**-8)]))[0] == -(1.0 + 2**-6)
+    # subnormal bf16 values sit on the grid 2^-133 (smallest normal 2^-126)
+    assert O.round_to_bf16(np.array([1.5 * 2.0**-133]))[0] == 2.0**-132      # halfway -> even
+    assert O.round_to_bf16(np.array([2.0**-134]))[0] == 0.0                   # halfway -> even (0)
+    assert O.round_to_bf16(np.array([2.0**-134 + 2.0**-160]))[0] == 2.0**-133
+    assert O.round_to_bf16(np.array([3 * 2.0**-130 + 2.0**-140]))[0] == 3 * 2.0**-130
 
 
 def test_round_to_bf16_matches_torch_on_float32():

@@ -299,6 +299,30 @@ int moe_layer(const moe_shape* shape, const void* x, const void* w_router,
               const moe_perm* perm, void* workspace, size_t workspace_bytes,
               hipStream_t stream);
 
+/* moe_layer for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same validation, kernels and results as moe_layer, with the workspace
+ * taken from a fixed device array inside the library instead of an argument.
+ * The call allocates nothing.  Each device holds one such array of
+ * MOE_NOALLOC_SCRATCH_BYTES from the first call on it until the process
+ * ends; its device address is looked up on that first call, so make the
+ * first call on a device outside graph capture.
+ *   - A shape whose moe_workspace_size exceeds MOE_NOALLOC_SCRATCH_BYTES is
+ *     rejected with MOE_E_WORKSPACE before any HIP call (at H = 2560,
+ *     E = 512, I = 640, top-10 that is T > ~800 tokens).
+ *   - `stream` must belong to the current device (MOE_E_DEVICE otherwise).
+ *   - Every call on one device shares that device's array: calls that may
+ *     overlap on one device (different streams, or host threads without
+ *     ordering) race and give undefined results.  Calls enqueued on one
+ *     stream are ordered and safe.  The array keeps the last call's contents;
+ *     the layer needs none of it initialised.
+ * Other arguments, outputs and error codes as moe_layer. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_layer_noalloc(const moe_shape* shape, const void* x, const void* w_router,
+                      const float* router_bias, const moe_experts* experts,
+                      const void* residual, void* out, int32_t* topk_ids, float* topk_w,
+                      const moe_perm* perm, hipStream_t stream);
+
 /* Stage the active experts' records into device memory (AFN-019,
  * "Hypothesis H5": a block reads the deduplicated union of its routes;
  * "Why overlap alone cannot defeat the byte roofline": exact bytes first).

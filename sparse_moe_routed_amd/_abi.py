@@ -28,7 +28,7 @@ EXPORTS = ("moe_workspace_size", "moe_status_str", "moe_tile_experts", "moe_rout
            "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_ffn_fused",
            "moe_ffn_fused_items", "moe_device_clock_khz", "moe_combine", "moe_layer",
            "moe_stage_experts", "moe_route_locality_blocks", "moe_route_locality",
-           "moe_stream_read")
+           "moe_stream_read", "moe_layer_noalloc")
 MOE_F_TILED_WEIGHTS = 0x1
 MOE_F_CHECK_FINITE = 0x2
 MOE_F_FUSED_FFN = 0x4
@@ -97,9 +97,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                       ctypes.c_uint32, vp]
     lib.moe_layer.argtypes = [P(moe_shape), vp, vp, vp, P(moe_experts), vp, vp, vp, vp,
                               P(moe_perm), vp, sz, vp]
+    lib.moe_layer_noalloc.argtypes = [P(moe_shape), vp, vp, vp, P(moe_experts), vp, vp, vp, vp,
+                                      P(moe_perm), vp]
     for name in ("moe_tile_experts", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_ffn_gate_up",
                  "moe_ffn_down", "moe_ffn_fused", "moe_device_clock_khz", "moe_combine", "moe_layer",
-                 "moe_route_locality", "moe_stage_experts", "moe_stream_read"):
+                 "moe_route_locality", "moe_stage_experts", "moe_stream_read", "moe_layer_noalloc"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -230,6 +232,18 @@ def moe_layer(shape, x, w_router, router_bias, experts, residual, out, topk_ids,
                           None if perm is None else ctypes.byref(perm), ptr(workspace),
                           workspace_bytes, stream_handle(stream))
     return _ret(st, "moe_layer", check)
+
+
+def moe_layer_noalloc(shape, x, w_router, router_bias, experts, residual, out, topk_ids, topk_w,
+                      perm, stream=None, check=True) -> int:
+    st = load().moe_layer_noalloc(ctypes.byref(shape), ptr(x), ptr(w_router), ptr(router_bias),
+                                  None if experts is None else ctypes.byref(experts), ptr(residual),
+                                  ptr(out), ptr(topk_ids), ptr(topk_w),
+                                  None if perm is None else ctypes.byref(perm), stream_handle(stream))
+    return _ret(st, "moe_layer_noalloc", check)
+
+
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def moe_stream_read(buf, nbytes, sink, stream=None, check=True) -> int:

@@ -263,6 +263,87 @@ static hipError_t ffn_and_combine(const moe_shape& s, const Plan& pl, const void
   return e;
 }
 
+int layer_call(const moe_shape* shape, const void* x, const void* w_router, const float* router_bias,
+               const moe_experts* experts, const void* residual, void* out, int32_t* topk_ids,
+               float* topk_w, const moe_perm* perm, void* workspace, size_t workspace_bytes,
+               hipStream_t stream, ScratchFn scratch) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if ((st = check_ptrs({x, w_router, out, topk_ids, topk_w}))) return st;
+  if ((st = check_opt_ptr(router_bias)) || (st = check_opt_ptr(residual))) return st;
+  if ((st = check_experts(s, experts))) return st;
+  if (perm && (st = check_perm(perm))) return st;
+  Plan pl;
+  make_plan(s, &pl);
+  // the no-allocation entry point supplies its own scratch once the call is valid
+  if (scratch && (st = scratch(pl.total, stream, &workspace, &workspace_bytes))) return st;
+  if ((st = check_ws(pl, workspace, workspace_bytes))) return st;
+  const size_t P = static_cast<size_t>(s.T) * s.top_k, ab = act_bytes(s);
+  Span outs[10];
+  outs[0] = {out, static_cast<size_t>(s.T) * s.H * ab};
+  outs[1] = {topk_ids, P * 4};
+  outs[2] = {topk_w, P * 4};
+  outs[3] = {workspace, pl.total};
+  int no = 4;
+  if (perm) {
+    perm_spans(s, *perm, outs + 4);
+    no = 10;
+  }
+  Span ins[10];
+  ins[0] = {x, static_cast<size_t>(s.T) * s.H * ab};
+  ins[1] = {w_router, static_cast<size_t>(s.E) * s.H * ab};
+  ins[2] = {router_bias, router_bias ? s.E * 4u : 0};
+  ins[3] = {residual, residual ? static_cast<size_t>(s.T) * s.H * ab : 0};
+  expert_spans(s, *experts, ins + 4);
+  if (any_alias(outs, no, ins, 10)) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  int32_t* tiles = ws_tiles(pl, workspace);
+  char* wsb = static_cast<char*>(workspace);
+  if (!(s.flags & MOE_F_CHECK_FINITE)) {
+    const PermPtrs pp = perm ? perm_ptrs(*perm) : ws_perm(s, pl, workspace);
+    hipError_t e = launch_route(s, pl, x, w_router, router_bias, topk_ids, topk_w, nullptr,
+                                workspace, stream);
+    if (e == hipSuccess) e = launch_permute(s, pl, topk_ids, pp, tiles, workspace, stream);
+    if (e == hipSuccess) e = ffn_and_combine(s, pl, x, *experts, pp, tiles, topk_w, residual, out, workspace, stream);
+    return device_status(e);
+  }
+  // private results (ids, weights, permutation, output), checked, then published
+  const PermPtrs wp = ws_perm(s, pl, workspace);
+  int32_t* pids = reinterpret_cast<int32_t*>(wsb + pl.ids_off);
+  float* pw = reinterpret_cast<float*>(wsb + pl.w_off);
+  void* pout = wsb + pl.out_off;
+  uint32_t* status = reinterpret_cast<uint32_t*>(wsb + pl.status_off);
+  const bool bf = s.act == MOE_DT_BF16;
+  const size_t TH = static_cast<size_t>(s.T) * s.H;
+  hipError_t e = launch_zero_status(status, stream);
+  if (e == hipSuccess) e = launch_check_finite(x, TH, bf, kBadX, status, stream);
+  if (e == hipSuccess)
+    e = launch_route(s, pl, x, w_router, router_bias, pids, pw, nullptr, workspace, stream);
+  if (e == hipSuccess)
+    e = launch_check_finite(wsb + pl.logits_off, static_cast<size_t>(s.T) * s.E, false, kBadLogits,
+                            status, stream);
+  if (e == hipSuccess) e = launch_permute(s, pl, pids, wp, tiles, workspace, stream);
+  if (e == hipSuccess) e = ffn_and_combine(s, pl, x, *experts, wp, tiles, pw, residual, pout, workspace, stream);
+  if (e == hipSuccess) e = launch_check_finite(pout, TH, bf, kBadOut, status, stream);
+  if ((st = finite_status(pl, workspace, stream, e))) return st;
+  e = publish(out, pout, TH * ab, stream);
+  if (e == hipSuccess) e = publish(topk_ids, pids, P * 4, stream);
+  if (e == hipSuccess) e = publish(topk_w, pw, P * 4, stream);
+  if (e == hipSuccess && perm) {
+    const PermPtrs cp = perm_ptrs(*perm);
+    e = publish(cp.counts, wp.counts, s.E * 4u, stream);
+    if (e == hipSuccess) e = publish(cp.offsets, wp.offsets, (s.E + 1) * 4u, stream);
+    if (e == hipSuccess) e = publish(cp.sorted_pair, wp.sorted_pair, P * 4, stream);
+    if (e == hipSuccess) e = publish(cp.pair_row, wp.pair_row, P * 4, stream);
+    if (e == hipSuccess) e = publish(cp.active, wp.active, s.E * 4u, stream);
+    if (e == hipSuccess) e = publish(cp.n_active, wp.n_active, 4, stream);
+  }
+  return device_status(e);
+}
+
+
 }  // namespace moe
 
 using namespace moe;
@@ -528,78 +609,8 @@ int moe_layer(const moe_shape* shape, const void* x, const void* w_router, const
               const moe_experts* experts, const void* residual, void* out, int32_t* topk_ids,
               float* topk_w, const moe_perm* perm, void* workspace, size_t workspace_bytes,
               hipStream_t stream) {
-  int st = check_shape(shape);
-  if (st) return st;
-  const moe_shape& s = *shape;
-  if (s.T == 0) return MOE_OK;
-  if ((st = check_ptrs({x, w_router, out, topk_ids, topk_w}))) return st;
-  if ((st = check_opt_ptr(router_bias)) || (st = check_opt_ptr(residual))) return st;
-  if ((st = check_experts(s, experts))) return st;
-  if (perm && (st = check_perm(perm))) return st;
-  Plan pl;
-  make_plan(s, &pl);
-  if ((st = check_ws(pl, workspace, workspace_bytes))) return st;
-  const size_t P = static_cast<size_t>(s.T) * s.top_k, ab = act_bytes(s);
-  Span outs[10];
-  outs[0] = {out, static_cast<size_t>(s.T) * s.H * ab};
-  outs[1] = {topk_ids, P * 4};
-  outs[2] = {topk_w, P * 4};
-  outs[3] = {workspace, pl.total};
-  int no = 4;
-  if (perm) {
-    perm_spans(s, *perm, outs + 4);
-    no = 10;
-  }
-  Span ins[10];
-  ins[0] = {x, static_cast<size_t>(s.T) * s.H * ab};
-  ins[1] = {w_router, static_cast<size_t>(s.E) * s.H * ab};
-  ins[2] = {router_bias, router_bias ? s.E * 4u : 0};
-  ins[3] = {residual, residual ? static_cast<size_t>(s.T) * s.H * ab : 0};
-  expert_spans(s, *experts, ins + 4);
-  if (any_alias(outs, no, ins, 10)) return MOE_E_ALIAS;
-  (void)hipGetLastError();
-  int32_t* tiles = ws_tiles(pl, workspace);
-  char* wsb = static_cast<char*>(workspace);
-  if (!(s.flags & MOE_F_CHECK_FINITE)) {
-    const PermPtrs pp = perm ? perm_ptrs(*perm) : ws_perm(s, pl, workspace);
-    hipError_t e = launch_route(s, pl, x, w_router, router_bias, topk_ids, topk_w, nullptr,
-                                workspace, stream);
-    if (e == hipSuccess) e = launch_permute(s, pl, topk_ids, pp, tiles, workspace, stream);
-    if (e == hipSuccess) e = ffn_and_combine(s, pl, x, *experts, pp, tiles, topk_w, residual, out, workspace, stream);
-    return device_status(e);
-  }
-  // private results (ids, weights, permutation, output), checked, then published
-  const PermPtrs wp = ws_perm(s, pl, workspace);
-  int32_t* pids = reinterpret_cast<int32_t*>(wsb + pl.ids_off);
-  float* pw = reinterpret_cast<float*>(wsb + pl.w_off);
-  void* pout = wsb + pl.out_off;
-  uint32_t* status = reinterpret_cast<uint32_t*>(wsb + pl.status_off);
-  const bool bf = s.act == MOE_DT_BF16;
-  const size_t TH = static_cast<size_t>(s.T) * s.H;
-  hipError_t e = launch_zero_status(status, stream);
-  if (e == hipSuccess) e = launch_check_finite(x, TH, bf, kBadX, status, stream);
-  if (e == hipSuccess)
-    e = launch_route(s, pl, x, w_router, router_bias, pids, pw, nullptr, workspace, stream);
-  if (e == hipSuccess)
-    e = launch_check_finite(wsb + pl.logits_off, static_cast<size_t>(s.T) * s.E, false, kBadLogits,
-                            status, stream);
-  if (e == hipSuccess) e = launch_permute(s, pl, pids, wp, tiles, workspace, stream);
-  if (e == hipSuccess) e = ffn_and_combine(s, pl, x, *experts, wp, tiles, pw, residual, pout, workspace, stream);
-  if (e == hipSuccess) e = launch_check_finite(pout, TH, bf, kBadOut, status, stream);
-  if ((st = finite_status(pl, workspace, stream, e))) return st;
-  e = publish(out, pout, TH * ab, stream);
-  if (e == hipSuccess) e = publish(topk_ids, pids, P * 4, stream);
-  if (e == hipSuccess) e = publish(topk_w, pw, P * 4, stream);
-  if (e == hipSuccess && perm) {
-    const PermPtrs cp = perm_ptrs(*perm);
-    e = publish(cp.counts, wp.counts, s.E * 4u, stream);
-    if (e == hipSuccess) e = publish(cp.offsets, wp.offsets, (s.E + 1) * 4u, stream);
-    if (e == hipSuccess) e = publish(cp.sorted_pair, wp.sorted_pair, P * 4, stream);
-    if (e == hipSuccess) e = publish(cp.pair_row, wp.pair_row, P * 4, stream);
-    if (e == hipSuccess) e = publish(cp.active, wp.active, s.E * 4u, stream);
-    if (e == hipSuccess) e = publish(cp.n_active, wp.n_active, 4, stream);
-  }
-  return device_status(e);
+  return layer_call(shape, x, w_router, router_bias, experts, residual, out, topk_ids, topk_w, perm,
+                    workspace, workspace_bytes, stream, nullptr);
 }
 
 // Device-usable address of a buffer the kernel will read: device memory as

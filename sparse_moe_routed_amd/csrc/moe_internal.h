@@ -48,6 +48,18 @@ struct Plan {
 
 bool make_plan(const moe_shape& s, Plan* p);
 
+// Supplies the workspace of a validated moe_layer call that received none:
+// `need` is the plan's size; on MOE_OK *ws / *ws_bytes describe device
+// memory of at least `need` bytes usable on `st`'s device.
+typedef int (*ScratchFn)(size_t need, hipStream_t st, void** ws, size_t* ws_bytes);
+
+// moe_layer with an optional scratch supplier (nullptr: the caller's
+// workspace); every validation step runs before `scratch` is called.
+int layer_call(const moe_shape* shape, const void* x, const void* w_router, const float* router_bias,
+               const moe_experts* experts, const void* residual, void* out, int32_t* topk_ids,
+               float* topk_w, const moe_perm* perm, void* workspace, size_t workspace_bytes,
+               hipStream_t stream, ScratchFn scratch);
+
 struct PermPtrs {
   int32_t *counts, *offsets, *sorted_pair, *pair_row, *active, *n_active;
 };

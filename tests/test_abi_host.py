@@ -281,3 +281,28 @@ def test_ffn_fused_validation():
     assert call(item_clock=b["out"].addr) == 6                               # clock over y
     assert call(workspace_bytes=16) == 7
     assert all(v.untouched() for v in b.values())
+
+
+def test_layer_noalloc_validation():
+    """moe_layer_noalloc validates like moe_layer and refuses a shape whose
+    workspace exceeds its fixed device array, all before any HIP call."""
+    b = bufs()
+    ex = M.make_experts(b["g"].addr, b["u"].addr, b["d"].addr)
+
+    def call(sh, **over):
+        a = dict(x=b["x"].addr, w_router=b["wr"].addr, router_bias=None, experts=ex, residual=None,
+                 out=b["out"].addr, topk_ids=b["ids"].addr, topk_w=b["w"].addr, perm=None)
+        a.update(over)
+        return M.moe_layer_noalloc(sh, stream=0, check=False, **a)
+
+    big = shape(T=4096)
+    assert M.moe_workspace_size(big) > M.MOE_NOALLOC_SCRATCH_BYTES
+    assert call(big) == 7                                    # MOE_E_WORKSPACE
+    assert call(shape(T=0)) == 0                             # no-op
+    assert call(shape(H=100)) == 2
+    assert call(shape(), x=None) == 1
+    assert call(shape(), out=b["out"].addr + 8) == 5
+    assert all(v.untouched() for v in b.values())
+    lib = M.load()
+    assert lib.moe_layer_noalloc(None, None, None, None, None, None, None, None, None, None,
+                                 None) == 1

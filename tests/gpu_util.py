@@ -120,7 +120,18 @@ def check_routes(ids_gpu, w_gpu, logits64, ids_ref, w_ref, k):
     return dict(mismatch=int(mism.sum()), near_ties=int(near.sum()), max_w_err=werr), ~mism
 
 
-def check_values(got64, ref64, act, what):
+def check_values(got64, ref64, act, what, scaled=False):
+    """max-abs and rel-L2 of GPU values against float64 oracle values.
+
+    scaled=True (rows whose scale grows beyond 1, as in the 48-layer residual
+    stacks, where the activations and with them the expert outputs grow layer
+    by layer): the bf16 max-abs bound holds at unit scale and is applied row
+    by row to max_n |got - ref| / max(1, rms(ref row)).  Rounding the bf16
+    intermediate and outputs gives errors proportional to the size of the
+    values (a bf16 value v alone is off by up to |v| * 2^-9, more than 2e-2
+    once |v| > 10.24), so a fixed absolute bound stops being attainable for
+    rows of a few units; for rows of rms <= 1 the scaled bound is the
+    absolute one."""
     got64 = np.asarray(got64, dtype=np.float64)
     ref64 = np.asarray(ref64, dtype=np.float64)
     assert got64.shape == ref64.shape
@@ -128,26 +139,47 @@ def check_values(got64, ref64, act, what):
     err = np.abs(got64 - ref64)
     mx = float(err.max()) if err.size else 0.0
     rl2 = float(np.linalg.norm(got64 - ref64) / max(np.linalg.norm(ref64), 1e-300)) if err.size else 0.0
+    out = dict(max_abs=mx, rel_l2=rl2)
     if act == "f32":
         assert mx <= TOL_F32_ABS, f"{what}: max-abs {mx} (rel-L2 {rl2})"
+    elif scaled:
+        r2 = ref64.reshape(-1, ref64.shape[-1]) if ref64.ndim else ref64.reshape(1, 1)
+        e2 = err.reshape(r2.shape)
+        row_rms = np.sqrt(np.mean(r2 ** 2, axis=1)) if r2.size else np.zeros(0)
+        ms = float((e2.max(axis=1) / np.maximum(1.0, row_rms)).max()) if r2.size else 0.0
+        rms = float(np.sqrt(np.mean(ref64 ** 2))) if err.size else 0.0
+        out["max_scaled"], out["rms_ref"] = ms, rms
+        assert ms <= TOL_BF16_ABS and rl2 <= TOL_BF16_RL2, \
+            f"{what}: max over rows of max-abs / max(1, row rms) = {ms} (max-abs {mx}, rms {rms}), rel-L2 {rl2}"
     else:
         assert mx <= TOL_BF16_ABS and rl2 <= TOL_BF16_RL2, f"{what}: max-abs {mx} rel-L2 {rl2}"
-    return dict(max_abs=mx, rel_l2=rl2)
+    return out
 
 
 def cxx_oracle_layer(case: Case, tokens=None):
     """The layer through the C++ float64 oracle on the case's input bytes,
     for all tokens or for the rows `tokens` (every step is per token except
     the row order of the permutation, so a subset gives those tokens' exact
-    outputs).
-
-    The host copies of the expert arrays are zero-filled (untouched pages
-    cost no memory) except the experts the routes select, which are copied
-    from the device; the numpy oracle's router names them."""
+    outputs).  The C++ oracle decodes the activation and router bytes itself
+    and its own router picks the experts whose weights are copied to the host
+    (the other experts' pages stay zero and are never read)."""
     from oracle import oracle_c as C
-    cfg, ex = case.cfg, case.li.experts
-    x64 = case.x64 if tokens is None else case.x64[np.asarray(tokens)]
-    need = np.unique(O.select_topk(O.router_logits(x64, case.wr64, case.bias64), cfg.k))
+    cfg = case.cfg
+    xs = np_of(case.li.x)
+    if tokens is not None:
+        xs = xs[np.asarray(tokens)]
+    x64 = C.decode_act_c(xs, cfg.act)
+    wr64 = C.decode_act_c(np_of(case.li.w_router), cfg.act)
+    need = np.unique(C.routes_c(x64, wr64, case.bias64, cfg.k)[1])
+    host = host_experts(case.li.experts, need)
+    res = x64 if cfg.residual else None
+    return C.moe_layer_c(x64, wr64, case.bias64, host, cfg.wfmt, cfg.act, cfg.k, res)
+
+
+def host_experts(ex: dict, need) -> dict:
+    """Host storage arrays of the expert tensors (row-major) with the experts
+    in `need` copied from the device and every other expert zero (untouched
+    pages cost no memory)."""
     host = {}
     for n, t in ex.items():
         if t is None:
@@ -158,5 +190,11 @@ def cxx_oracle_layer(case: Case, tokens=None):
         for e in need:
             a[int(e)] = tensor_to_numpy_storage(t[int(e)])
         host[n] = a
-    res = x64 if cfg.residual else None
-    return C.moe_layer_c(x64, case.wr64, case.bias64, host, cfg.wfmt, cfg.act, cfg.k, res)
+    return host
+
+
+def check_oracles_agree(ids_numpy, ids_cxx, logits64, k):
+    """The two oracles' routes: identical outside near-tie tokens."""
+    near = O.near_tie_tokens(logits64, k)
+    bad = (np.asarray(ids_numpy) != np.asarray(ids_cxx)).any(axis=1) & ~near
+    assert not bad.any(), f"numpy and C++ oracle routes differ on tokens {np.nonzero(bad)[0][:8]}"

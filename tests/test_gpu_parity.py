@@ -12,8 +12,8 @@ import torch
 import sparse_moe_routed_amd as M
 from moe_inputs import CONFIGS, make_x
 from oracle import moe_oracle as O
-from tests.gpu_util import (DEV, buffers, check_routes, check_values, decode, i32, make_case, np_of,
-                            say, tiled_ok, to_act_tensor)
+from tests.gpu_util import (DEV, buffers, check_oracles_agree, check_routes, check_values, decode, i32,
+                            make_case, np_of, say, tiled_ok, to_act_tensor)
 
 pytestmark = pytest.mark.gpu
 
@@ -222,6 +222,8 @@ def test_layer_against_cxx_oracle(name, full):
     cfg = case.cfg
     say(f"[cxx {name}] C++ oracle: {cfg}")
     ref = cxx_oracle_layer(case)
+    check_oracles_agree(O.select_topk(O.router_logits(case.x64, case.wr64, case.bias64), cfg.k),
+                        ref.ids, ref.logits, cfg.k)
     res = case.li.x if cfg.residual else None
     for tiled in (False, True) if tiled_ok(cfg) else (False,):
         buf = buffers(cfg, tiled)
@@ -246,6 +248,8 @@ def test_full_layer_sampled_against_cxx_oracle(name, cfg, layer):
     sample = np.sort(np.random.default_rng(77 + layer).choice(cfg.T, size=32, replace=False))
     say(f"[cxx full {name} layer {layer}] C++ oracle on 32 tokens")
     ref = cxx_oracle_layer(case, sample)
+    check_oracles_agree(O.select_topk(O.router_logits(case.x64[sample], case.wr64, case.bias64),
+                                      cfg.k), ref.ids, ref.logits, cfg.k)
     buf = buffers(cfg, tiled_ok(cfg))
     res = case.li.x if cfg.residual else None
     say(f"[cxx full {name} layer {layer}] moe_layer")

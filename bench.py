@@ -10,8 +10,13 @@ as it does between decode batches.
 
 Prints one JSON line: tokens/s of the workload, the roofline of the dominant
 kernel (the grouped gate/up + SwiGLU kernel, timed with HIP events around
-each of its launches on the stream it runs on), and the two CPU oracles
-(float64 numpy, float64 C++) timed on bounded samples of the same workload.
+each of its launches on the stream it runs on), the CPU oracles timed on
+bounded samples of the same workload (`cpu_baseline`: the plain C++ float64
+oracle; `cpu_baseline_numpy`: the numpy float64 oracle) and the GPU routes of
+layer 0 checked against the C++ oracle (`oracle_route_check`: mismatches,
+near ties, largest logit difference).  With no --workload the headline line
+is the decode workload and the other four workloads follow under
+`workloads`, each measured the same way in the same process.
 """
 from __future__ import annotations
 
@@ -47,7 +52,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default: 200 for one layer, 10 for 48-layer stacks)")
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode", choices=list(WORKLOADS))
+    ap.add_argument("--workload", default=None, choices=list(WORKLOADS),
+                    help="one workload only (default: decode as the headline line, the other "
+                         "workloads measured after it under `workloads`)")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="with no --workload: measure decode only")
     ap.add_argument("--batches", type=int, default=16, help="distinct token batches cycled")
     ap.add_argument("--layers", type=int, default=None, help="override the stack depth")
     ap.add_argument("--tokens", type=int, default=None,
@@ -55,7 +64,10 @@ def parse():
     ap.add_argument("--layout", default="tiled", choices=["tiled", "row"],
                     help="expert weight layout (tiled: converted once at load time)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="oracle sample budget of the headline workload (per oracle)")
+    ap.add_argument("--cpu-seconds-other", type=float, default=6.0,
+                    help="C++ oracle sample budget of each other workload in the default run")
     ap.add_argument("--flush-mib", type=int, default=0,
                     help="read this many MiB of scratch between timed steps (evicts L2/MALL with "
                          "clean lines); each step is then timed on its own and value = tokens / sum "
@@ -128,14 +140,20 @@ def weight_bytes_per_param(cfg):
 
 def gateup_traffic(cfg, U):
     """Algorithmic bytes and flops of one grouped gate/up launch: the gate and
-    up weights of the U active experts read once, the T token rows read, the
-    P x I intermediate written."""
+    up weights of the U active experts read once and the T token rows read.
+    The P x I SwiGLU intermediate it writes is scratch of the implementation
+    (the next kernel reads it back) and is not counted."""
     act = 4 if cfg.act == "f32" else 2
     P = cfg.T * cfg.k
     w = U * 2 * cfg.I * cfg.H * weight_bytes_per_param(cfg)
-    b = w + cfg.T * cfg.H * act + P * cfg.I * act
+    b = w + cfg.T * cfg.H * act
     f = 2.0 * P * 2 * cfg.I * cfg.H
     return b, f
+
+
+# tokens of layer 0 (over the cycled batches) whose GPU routes the CPU leg
+# checks against the C++ oracle
+ROUTE_CHECK_MAX_TOKENS = 16384
 
 
 def layer_bytes(cfg, U):
@@ -203,7 +221,6 @@ def main():
     import torch
 
     import sparse_moe_routed_amd as M
-    from moe_inputs import CONFIGS, make_experts, make_router, make_x
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
@@ -220,16 +237,50 @@ def main():
         return
 
     M.load()
-    cfg = CONFIGS[WORKLOADS[args.workload]]
-    if args.workload in WORKLOAD_TOKENS:
-        cfg = cfg.with_(name=args.workload, T=WORKLOAD_TOKENS[args.workload])
-    if args.tokens is not None:
+    headline = args.workload or "decode"
+    line = run_workload(args, M, torch, dev, headline, headline=True)
+    if args.workload is None and not args.only_headline:
+        # the default run also measures the other workloads, each with its own
+        # weights, in this process after the headline one (its memory freed)
+        line["workloads"] = {}
+        for wl in OTHER_WORKLOADS:
+            line["workloads"][wl] = summarize(run_workload(args, M, torch, dev, wl, headline=False))
+        line["workloads_note"] = (
+            "each workload as its own run of the same steps/warmup in this process: tokens/s, "
+            "step time, whole-layer HBM fraction, the dominant kernel's roofline, HIP-graph "
+            "replay, the C++ float64 oracle timed on the host cores and the oracle route check")
+    print(json.dumps(line))
+
+
+OTHER_WORKLOADS = ("tiny", "prefill", "stack_int4", "verify_int2")
+
+
+def summarize(r):
+    """The fields of one workload's line kept under `workloads` in the default run."""
+    keep = ("value", "unit", "steps", "warmup", "ms_per_step", "dtype", "config", "timing",
+            "layer_hbm", "graph", "cpu_baseline", "oracle_route_check")
+    out = {k: r[k] for k in keep if k in r}
+    rf = r["roofline"]
+    out["roofline"] = {k: rf[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic",
+                                          "kernel", "avg_launch_us", "hbm_frac", "mfma_frac",
+                                          "attainable_frac")}
+    return out
+
+
+def run_workload(args, M, torch, dev, name, headline):
+    """One workload end to end: inputs resident in HBM, untimed routing
+    statistics, warmup, the timed steps, the dominant-kernel roofline, graph
+    replay, and the CPU-oracle leg.  Returns the JSON line as a dict."""
+    from moe_inputs import CONFIGS, make_experts, make_router, make_x
+
+    cfg = CONFIGS[WORKLOADS[name]]
+    if name in WORKLOAD_TOKENS:
+        cfg = cfg.with_(name=name, T=WORKLOAD_TOKENS[name])
+    if args.tokens is not None and headline:
         cfg = cfg.with_(T=args.tokens)
-    L = cfg.layers if args.layers is None else args.layers
-    if args.steps is None:
-        args.steps = 200 if L == 1 else 10
-    if args.warmup is None:
-        args.warmup = 20 if L == 1 else 3
+    L = cfg.layers if (args.layers is None or not headline) else args.layers
+    steps = args.steps if args.steps is not None else (200 if L == 1 else 10)
+    warmup = args.warmup if args.warmup is not None else (20 if L == 1 else 3)
     T, k = cfg.T, cfg.k
 
     # ---- inputs resident in HBM --------------------------------------------
@@ -255,33 +306,41 @@ def main():
     acts = [torch.empty_like(xs[0]) for _ in range(2)]
     torch.cuda.synchronize()
 
-    ev_a = [TimingEvent() for _ in range(args.steps * L)]
-    ev_b = [TimingEvent() for _ in range(args.steps * L)]
+    ev_a = [TimingEvent() for _ in range(steps * L)]
+    ev_b = [TimingEvent() for _ in range(steps * L)]
 
+    # one layer = moe_route_permute -> moe_ffn_gate_up -> moe_ffn_down_combine
+    # (the same kernels as moe_layer; the gate/up call is separate so that the
+    # dominant kernel can be timed on its own)
     def step(i, timed_idx=None):
         x = xs[i % len(xs)]
         for l, (wr, bias, _, exg) in enumerate(layers):
             out = acts[l % 2] if L > 1 else buf.out
-            buf.route(x, wr, bias, logits=False)
-            buf.permute()
+            buf.route_permute(x, wr, bias, logits=False)
             if timed_idx is not None:
                 ev_a[timed_idx * L + l].record()
             buf.ffn_gate_up(x, exg)
             if timed_idx is not None:
                 ev_b[timed_idx * L + l].record()
-            buf.ffn_down(exg)
-            buf.combine(residual=x if cfg.residual else None, out=out)
+            buf.ffn_down_combine(exg, residual=x if cfg.residual else None, out=out)
             x = out
 
     # ---- routing statistics per (batch, layer), untimed ---------------------
+    # (layer 0 also keeps the GPU routes and float32 logits of every batch for
+    # the oracle route check of the CPU leg; its inputs come from the generator)
     U = np.zeros((len(xs), L), dtype=np.int64)
     loc = {"overlap": [], "blocks": {B: [] for B in range(1, 6)}, "skew": []}
+    gpu_routes = []
+    check_tokens = 0
     for b in range(len(xs)):
         x = xs[b]
         for l, (wr, bias, _, exg) in enumerate(layers):
             out = acts[l % 2] if L > 1 else buf.out
-            buf.route(x, wr, bias, logits=False)
-            buf.permute()
+            keep = l == 0 and check_tokens + T <= ROUTE_CHECK_MAX_TOKENS
+            buf.route_permute(x, wr, bias, logits=keep)
+            if keep:
+                gpu_routes.append((b, buf.topk_ids.cpu().numpy(), buf.logits.cpu().numpy()))
+                check_tokens += T
             U[b, l] = int(buf.n_active.item())
             ov, blocks = buf.route_locality()
             loc["overlap"].append(ov[1:].float().mean().item() if T > 1 else 0.0)
@@ -291,12 +350,11 @@ def main():
                     loc["blocks"][B].append(full.float().mean().item())
             loc["skew"].append(int(buf.counts.max().item()) / (T * k / cfg.E))
             buf.ffn_gate_up(x, exg)
-            buf.ffn_down(exg)
-            buf.combine(residual=x if cfg.residual else None, out=out)
+            buf.ffn_down_combine(exg, residual=x if cfg.residual else None, out=out)
             x = out
     torch.cuda.synchronize()
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     # Back to back: one event before the first and after the last step, and the
@@ -305,18 +363,19 @@ def main():
     # so the steps carry only the two around the dominant kernel).  Flushing:
     # one event before and one after each step, so that the flush between
     # steps is outside the step times.
-    ev_beg = [TimingEvent() for _ in range(args.steps + 1 if args.flush_mib else 2)]
-    ev_end = [TimingEvent() for _ in range(args.steps)] if args.flush_mib else None
+    flush = args.flush_mib if headline else 0
+    ev_beg = [TimingEvent() for _ in range(steps + 1 if flush else 2)]
+    ev_end = [TimingEvent() for _ in range(steps)] if flush else None
     scratch = sink = None
-    if args.flush_mib:
-        scratch = torch.zeros(args.flush_mib << 20, dtype=torch.uint8, device=dev)
+    if flush:
+        scratch = torch.zeros(flush << 20, dtype=torch.uint8, device=dev)
         sink = torch.zeros(1, dtype=torch.int32, device=dev)
         M.moe_stream_read(scratch, scratch.numel(), sink)
         torch.cuda.synchronize()
     wall0 = time.perf_counter()
     if scratch is None:
         ev_beg[0].record()
-    for i in range(args.steps):
+    for i in range(steps):
         if scratch is not None:
             ev_beg[i].record()
         step(i, timed_idx=i)
@@ -328,20 +387,20 @@ def main():
     wall = time.perf_counter() - wall0
     if scratch is None:
         elapsed_ms = ev_beg[0].elapsed_time(ev_beg[-1])
-        step_ms = np.array([ev_a[i * L].elapsed_time(ev_a[(i + 1) * L]) for i in range(args.steps - 1)]
-                           if args.steps > 1 else [elapsed_ms])
+        step_ms = np.array([ev_a[i * L].elapsed_time(ev_a[(i + 1) * L]) for i in range(steps - 1)]
+                           if steps > 1 else [elapsed_ms])
     else:
-        step_ms = np.array([ev_beg[i].elapsed_time(ev_end[i]) for i in range(args.steps)])
+        step_ms = np.array([ev_beg[i].elapsed_time(ev_end[i]) for i in range(steps)])
         elapsed_ms = float(step_ms.sum())
-    ms_per_step = elapsed_ms / args.steps
-    tokens_per_s = T * args.steps / (elapsed_ms / 1e3)
+    ms_per_step = elapsed_ms / steps
+    tokens_per_s = T * steps / (elapsed_ms / 1e3)
     del scratch, sink
 
     # ---- dominant kernel roofline --------------------------------------------
     gu_ms = np.array([a.elapsed_time(b) for a, b in zip(ev_a, ev_b)])
-    gu_bytes = np.zeros(args.steps * L)
-    gu_flops = np.zeros(args.steps * L)
-    for i in range(args.steps):
+    gu_bytes = np.zeros(steps * L)
+    gu_flops = np.zeros(steps * L)
+    for i in range(steps):
         for l in range(L):
             gu_bytes[i * L + l], gu_flops[i * L + l] = gateup_traffic(cfg, U[i % len(xs), l])
     avg_ms = float(gu_ms.mean())
@@ -358,10 +417,10 @@ def main():
         bound, peak, unit = "hbm", HBM_PEAK_GBS, "GB/s"
         achieved = avg_bytes / (avg_ms / 1e3) / 1e9
     digest = kernel_source_digest()
-    traffic = traffic_from_profiles(args.workload, digest)
+    traffic = traffic_from_profiles(name, digest)
 
     step_bytes = np.mean([sum(layer_bytes(cfg, U[b, l]) for l in range(L)) for b in range(len(xs))])
-    graph = None if args.no_graph else graph_replay(torch, buf, layers, xs, acts, cfg, L, args.steps)
+    graph = None if args.no_graph else graph_replay(torch, buf, layers, xs, acts, cfg, L, steps)
     # route-locality kernel time (on the last routes)
     la, lb = TimingEvent(), TimingEvent()
     buf.route_locality()
@@ -379,24 +438,32 @@ def main():
         "mean_skew_max_over_mean_load": round(float(np.mean(loc["skew"])), 2),
         "kernel_us": round(la.elapsed_time(lb) / 20 * 1e3, 2),
     }
-    probe = read_probe(M, dev, args.probe_mib) if args.probe_mib else None
-    off = None if args.no_offload else offload(M, torch, dev, cfg, layers, xs, buf, args.offload_steps)
-    fw = None if (args.no_fused or not tiled or T * k > 16384) else fused_waves(M, torch, dev, cfg, layers, xs)
+    probe = read_probe(M, dev, args.probe_mib) if (args.probe_mib and headline) else None
+    off = None if (args.no_offload or not headline) else offload(M, torch, dev, cfg, layers, xs, buf,
+                                                                 args.offload_steps)
+    fw = (None if (args.no_fused or not tiled or T * k > 16384 or not headline)
+          else fused_waves(M, torch, dev, cfg, layers, xs))
 
-    # ---- CPU oracle on a bounded sample --------------------------------------
-    cpu = cpu_cxx = None
+    # ---- CPU leg: the oracles on bounded samples, and the route check --------
+    cpu = cpu_np = check = None
+    del buf, acts
     if not args.no_cpu_baseline:
-        del buf
-        cpu = cpu_baseline(cfg, L, layers, xs, args.cpu_seconds, dev)
-        cpu_cxx = cpu_baseline_cxx(cfg, L, layers, xs, args.cpu_seconds, dev)
+        budget = args.cpu_seconds if headline else args.cpu_seconds_other
+        check = oracle_route_check(cfg, layers, xs, gpu_routes)
+        cpu = cpu_baseline_cxx(cfg, L, layers, xs, budget, dev)
+        if headline:
+            cpu_np = cpu_baseline(cfg, L, layers, xs, budget, dev)
+    n_batches = len(xs)
+    del layers, xs
+    torch.cuda.empty_cache()
 
-    line = {
+    return {
         "metric": "routed-MoE layer tokens/s",
         "value": round(tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -406,7 +473,7 @@ def main():
         "config": {"workload": cfg.name, "T": T, "H": cfg.H, "E": cfg.E, "I": cfg.I, "top_k": k,
                    "layers": L, "weights": cfg.wfmt if cfg.wfmt != "dense" else cfg.act,
                    "weight_layout": "tiled" if tiled else "row-major",
-                   "batches_cycled": len(xs), "parallelism": "none (1 GPU)"},
+                   "batches_cycled": n_batches, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": "k_gateup (grouped gate/up + SwiGLU)",
@@ -425,8 +492,8 @@ def main():
                          max(avg_flops / ((FP32_PEAK_TFLOPS if cfg.act == "f32" else BF16_PEAK_TFLOPS) * 1e12),
                              avg_bytes / (HBM_PEAK_GBS * 1e9)) / (avg_ms / 1e3), 4)},
         "timing": {"mode": ("steps back to back (per-step times between consecutive steps' "
-                             "first gate/up start events)" if not args.flush_mib else
-                            f"{args.flush_mib} MiB scratch read between steps, excluded"),
+                             "first gate/up start events)" if not flush else
+                            f"{flush} MiB scratch read between steps, excluded"),
                    "step_ms_median": round(float(np.median(step_ms)), 5),
                    "step_ms_p10": round(float(np.percentile(step_ms, 10)), 5),
                    "step_ms_p90": round(float(np.percentile(step_ms, 90)), 5)},
@@ -439,10 +506,10 @@ def main():
         "offload": off,
         "fused_waves": fw,
         "cpu_baseline": cpu,
-        "cpu_baseline_cxx": cpu_cxx,
+        "cpu_baseline_numpy": cpu_np,
+        "oracle_route_check": check,
         "host_wall_s": round(wall, 3),
     }
-    print(json.dumps(line))
 
 
 def graph_replay(torch, buf, layers, xs, acts, cfg, L, steps):
@@ -461,11 +528,10 @@ def graph_replay(torch, buf, layers, xs, acts, cfg, L, steps):
                     x = xs[b]
                     for l, (wr, bias, _, exg) in enumerate(layers):
                         out = acts[l % 2] if L > 1 else buf.out
-                        buf.route(x, wr, bias, logits=False, stream=s)
-                        buf.permute(stream=s)
+                        buf.route_permute(x, wr, bias, logits=False, stream=s)
                         buf.ffn_gate_up(x, exg, stream=s)
-                        buf.ffn_down(exg, stream=s)
-                        buf.combine(residual=x if cfg.residual else None, out=out, stream=s)
+                        buf.ffn_down_combine(exg, residual=x if cfg.residual else None, out=out,
+                                             stream=s)
                         x = out
                 graphs.append(g)
         torch.cuda.current_stream().wait_stream(s)
@@ -724,25 +790,62 @@ def cpu_baseline(cfg, L, layers, xs, budget_s, dev):
     per_layer = wall / len(layer_s)
     tcpu = min(cfg.T, 4096)
     return {"value": round(tcpu / (per_layer * L), 3), "unit": "tokens/s",
-            "cores": threads, "avg_busy_threads": round(cpu_t / wall, 2), "kind": "oracle",
+            "cores": threads, "avg_busy_threads": round(cpu_t / wall, 2), "kind": "oracle (numpy)",
             "sample": f"{len(layer_s)} layer passes of {tcpu}"
                       f"{'' if tcpu == cfg.T else ' of the ' + str(cfg.T)} tokens (float64 numpy oracle, "
                       f"{'extrapolated to ' + str(L) + ' layers' if L > 1 else 'whole layer'}); "
                       f"host copies of the selected experts excluded"}
 
 
+def oracle_route_check(cfg, layers, xs, gpu_routes):
+    """GPU routes of layer 0 against the C++ float64 oracle, on the generator's
+    bytes of every recorded batch (x, router weight, bias): expert IDs must
+    match exactly except on near-tie tokens (the oracle's k+1 best logits have
+    an adjacent gap below 1e-6 relative), which are counted separately; the
+    GPU's float32 logits are compared with the oracle's float64 logits."""
+    from moe_inputs import tensor_to_numpy_storage as npy
+    from oracle import moe_oracle as O
+    from oracle import oracle_c as C
+
+    if not gpu_routes:
+        return None
+    wr, bias, _, _ = layers[0]
+    wr64 = C.decode_act_c(npy(wr), cfg.act)
+    b64 = None if bias is None else bias.double().cpu().numpy()
+    n = mism = bad = near = 0
+    dmax = rmax = 0.0
+    t0 = time.perf_counter()
+    for b, ids_gpu, lg_gpu in gpu_routes:
+        x64 = C.decode_act_c(npy(xs[b]), cfg.act)
+        lg, ids, _, _ = C.routes_c(x64, wr64, b64, cfg.k)
+        nt = O.near_tie_tokens(lg, cfg.k)
+        mm = (ids_gpu != ids).any(axis=1)
+        n += len(ids)
+        mism += int(mm.sum())
+        bad += int((mm & ~nt).sum())
+        near += int(nt.sum())
+        d = np.abs(lg_gpu.astype(np.float64) - lg)
+        dmax = max(dmax, float(d.max()))
+        rmax = max(rmax, float((d / np.maximum(np.abs(lg), 1e-30)).max()))
+    return {"tokens": n, "layer": 0, "batches": len(gpu_routes), "mismatched_tokens": mism,
+            "mismatches_outside_near_ties": bad, "near_tie_tokens": near,
+            "max_abs_dlogit": dmax, "max_rel_dlogit": rmax,
+            "oracle": "C++ float64 (routes_c) on the generator's bytes",
+            "seconds": round(time.perf_counter() - t0, 2)}
+
+
 def cpu_baseline_cxx(cfg, L, layers, xs, budget_s, dev):
     """The plain C++ float64 oracle (oracle/moe_oracle_c.cpp), untuned, on a
     bounded sample: the first min(T, 64) tokens of each batch through the
-    first layer(s) until the budget is spent, extrapolated per layer like
-    cpu_baseline.  Its inputs are host copies of the batch and of the experts
-    the sample selects (the others stay zero pages); copies are not timed.
-    One thread per output row, all host cores."""
+    first layer(s) until the budget is spent, extrapolated per layer (tokens/s
+    = tokens / (mean seconds per layer * layers)).  Its inputs are host copies
+    of the batch (decoded by the C++ oracle) and of the experts its own router
+    selects for the sample (the others stay zero pages); copies are not
+    timed.  One thread per output row, all host cores."""
     import torch
 
     from moe_inputs import make_experts
     from moe_inputs import tensor_to_numpy_storage as npy
-    from oracle import moe_oracle as O
     from oracle import oracle_c as C
 
     threads = os.cpu_count() or 1
@@ -750,13 +853,13 @@ def cpu_baseline_cxx(cfg, L, layers, xs, budget_s, dev):
     layer_s = []
     t_budget = time.perf_counter()
     for b in range(len(xs)):
-        x64 = O.decode_act(npy(xs[b][:tcpu]), cfg.act)
+        x64 = C.decode_act_c(npy(xs[b][:tcpu]), cfg.act)
         for l in range(L):
             wr, bias, _, _ = layers[l]
             ex = make_experts(cfg, l, dev)
-            wr64 = O.decode_act(npy(wr), cfg.act)
+            wr64 = C.decode_act_c(npy(wr), cfg.act)
             b64 = None if bias is None else bias.double().cpu().numpy()
-            need = np.unique(O.select_topk(O.router_logits(x64, wr64, b64), cfg.k))
+            need = np.unique(C.routes_c(x64, wr64, b64, cfg.k, threads=threads)[1])
             host = {}
             for n, t in ex.items():
                 if t is None:
@@ -773,7 +876,8 @@ def cpu_baseline_cxx(cfg, L, layers, xs, budget_s, dev):
             r = C.moe_layer_c(x64, wr64, b64, host, cfg.wfmt, cfg.act, cfg.k,
                               x64 if cfg.residual else None, threads=threads)
             layer_s.append(time.perf_counter() - t0)
-            x64 = O.act_round(r.out, cfg.act)
+            x64 = (C.decode_act_c(C.round_bf16_c(r.out), "bf16") if cfg.act == "bf16"
+                   else r.out.astype(np.float32).astype(np.float64))
             if time.perf_counter() - t_budget > budget_s:
                 break
         if time.perf_counter() - t_budget > budget_s:

@@ -27,9 +27,11 @@
  *   owned by the caller; the library never allocates device memory.  Scratch
  *   memory is the caller's workspace of at least moe_workspace_size(shape)
  *   bytes (NULL allowed when that is 0); its contents need no initialisation.
- *   Between calls a workspace carries only the FFN tile plan (from
- *   moe_permute to moe_ffn_gate_up / moe_ffn_down); the library keeps no
- *   other state.
+ *   Between calls a workspace carries only the FFN tile plan and the
+ *   arrival counters of the single-launch paths, both written by the
+ *   library's own kernels (from moe_permute / moe_route_permute to
+ *   moe_ffn_gate_up / moe_ffn_down / moe_ffn_down_combine); the library
+ *   keeps no other state.
  * - Every call only ENQUEUES work on `stream` (NULL = the null stream) and
  *   returns without synchronizing.  Calls on different streams with disjoint
  *   outputs and workspaces are independent.
@@ -37,8 +39,10 @@
  * - Validation is complete before anything is enqueued: a non-MOE_OK return
  *   means no kernel was launched and no output byte was written
  *   (fail-closed, the rule of AFN-001 section "Phase 3: reject before the
- *   GPU exists").  MOE_E_DEVICE reports a HIP launch error; device faults
- *   surface at the caller's next synchronization.
+ *   GPU exists").  MOE_E_DEVICE reports a HIP error while enqueuing; a fault of
+ *   a kernel already enqueued is reported by the HIP runtime at the caller's
+ *   next synchronization (a GPU memory fault ends the process), not by a
+ *   later call of this library.
  * - Index tensors are int32; weights and logits are float32.
  *
  * Domain (MOE_E_SHAPE / MOE_E_LIMIT otherwise):
@@ -194,7 +198,11 @@ size_t moe_workspace_size(const moe_shape* shape);
 /* Static description of a status code; never NULL. */
 const char* moe_status_str(int status);
 
-/* Router: logits[t][e] = sum_h x[t][h] * w_router[e][h] + bias[e], then the
+/* Router (AFN-001, section "Phase 1: separate math from acceleration":
+ * float32 router softmax and normalized top-k; AFN-017, section "Tie
+ * handling belongs to membership"; AFN-021, section "The key equivalence --
+ * and where it breaks": exact IDs in rank order):
+ * logits[t][e] = sum_h x[t][h] * w_router[e][h] + bias[e], then the
  * top_k experts of each token by (logit descending, expert index ascending),
  * emitted in rank order, and their weights w[t][j] = exp(l_j - l_0) /
  * sum_i exp(l_i - l_0) over the selected logits (equal to the full float32
@@ -212,7 +220,8 @@ int moe_route(const moe_shape* shape, const void* x, const void* w_router,
               hipStream_t stream);
 
 /* Stable grouping of the pairs by expert (the permutation described at
- * moe_perm).  Also writes the grouped-FFN tile plan into the workspace (read
+ * moe_perm; AFN-019, section "Why overlap alone cannot defeat the byte
+ * roofline": token rows grouped by expert, repeated routes read once).  Also writes the grouped-FFN tile plan into the workspace (read
  * by moe_ffn_gate_up and moe_ffn_down).  topk_ids [T][top_k]: every entry in [0, E) and the top_k
  * entries of one token distinct (as moe_route produces); other inputs are
  * memory-safe but give an unspecified permutation. */
@@ -220,7 +229,23 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids,
                 const moe_perm* perm, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
-/* Grouped SwiGLU experts.  For every row r of expert e with pair p =
+/* moe_route followed by moe_permute (same outputs as the two calls, with
+ * `perm` receiving the permutation and the workspace the FFN tile plan), in
+ * as few launches as the shape allows: for bf16 batches of up to 32 tokens
+ * the top-k kernel's last workgroup builds the permutation, so routing and
+ * grouping take two kernel launches instead of three (AFN-019, "Why overlap
+ * alone cannot defeat the byte roofline": rows grouped by expert, repeated
+ * routes deduplicated).  Arguments as moe_route, plus perm (outputs). */
+int moe_route_permute(const moe_shape* shape, const void* x, const void* w_router,
+                      const float* router_bias, int32_t* topk_ids, float* topk_w, float* logits,
+                      const moe_perm* perm, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Grouped SwiGLU experts (AFN-019, section "Why overlap alone cannot defeat
+ * the byte roofline": gate [I x H] + up [I x H] + down [H x I] per expert;
+ * section "Hypothesis H4": gate and up together, down once the intermediate
+ * exists, a separate result slot per (token, expert)).  For every row r of
+ * expert e with pair p =
  * sorted_pair[r] and token t = p / top_k:
  *   y[r][n] = sum_i W_down[e][n][i] * silu(g_i) * u_i,
  *   g_i = sum_h W_gate[e][i][h] x[t][h],  u_i = sum_h W_up[e][i][h] x[t][h].
@@ -249,6 +274,21 @@ int moe_ffn_gate_up(const moe_shape* shape, const void* x,
 int moe_ffn_down(const moe_shape* shape, const void* h,
                  const moe_experts* experts, void* y, void* workspace,
                  size_t workspace_bytes, hipStream_t stream);
+
+/* moe_ffn_down followed by moe_combine: out[t][n] = residual[t][n] +
+ * sum_{j ascending} topk_w[t][j] * y_(t,j)[n] with y_(t,j) = W_down[e] h of
+ * the pair's row (AFN-019, "Hypothesis H4": separate result slots, the
+ * weighted sum in route-rank order).  The expert outputs y stay in the
+ * workspace.  With 16-row tiles (the plan's choice while T*top_k <= 12*E or
+ * T <= 16) of tiled weights the down kernel writes y in pair order, so the
+ * combine reads a token's slots without the pair -> row lookup.  The result
+ * equals moe_ffn_down + moe_combine bit for bit.  Reads the tile plan left by moe_permute (or
+ * moe_route_permute) for this shape and workspace; perm supplies
+ * sorted_pair and pair_row; h [P][I] act as from moe_ffn_gate_up; topk_w
+ * [T][top_k]; residual [T][H] act or NULL; out [T][H] act. */
+int moe_ffn_down_combine(const moe_shape* shape, const void* h, const moe_experts* experts,
+                         const moe_perm* perm, const float* topk_w, const void* residual, void* out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The grouped SwiGLU experts (same y as moe_grouped_ffn, up to float
  * rounding order) as one kernel of component waves (AFN-019, "Hypothesis
@@ -280,7 +320,9 @@ size_t moe_ffn_fused_items(const moe_shape* shape);
  * millisecond), for item_clock. */
 int moe_device_clock_khz(int32_t* khz);
 
-/* Route-rank-order combine: out[t][n] = residual[t][n] +
+/* Route-rank-order combine (AFN-019, section "Hypothesis H4": the weighted
+ * sum of the separate result slots in a fixed route-rank order):
+ * out[t][n] = residual[t][n] +
  * sum_{j=0}^{top_k-1} topk_w[t][j] * y[pair_row[t*top_k+j]][n], accumulated
  * in float32 with j ascending, rounded once to the act type.
  *   y [P][H] act; pair_row [P]; topk_w [T][top_k]; residual [T][H] act or
@@ -289,8 +331,11 @@ int moe_combine(const moe_shape* shape, const void* y, const int32_t* pair_row,
                 const float* topk_w, const void* residual, void* out,
                 hipStream_t stream);
 
-/* The whole layer: moe_route -> moe_permute -> moe_grouped_ffn ->
- * moe_combine with the same semantics, enqueued back to back.  perm may be
+/* The whole layer (the passages cited at the four calls; layers in sequence,
+ * x_{l+1} = x_l + moe_l(x_l) with residual = x: AFN-019, section "Hypothesis
+ * H6"): moe_route -> moe_permute -> moe_grouped_ffn -> moe_combine with the
+ * same semantics, enqueued back to back (as moe_route_permute ->
+ * moe_ffn_gate_up -> moe_ffn_down_combine).  perm may be
  * NULL (the permutation then lives in the workspace); residual may be NULL;
  * topk_ids/topk_w are outputs.  out must not overlap x or residual. */
 int moe_layer(const moe_shape* shape, const void* x, const void* w_router,

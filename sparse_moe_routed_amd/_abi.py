@@ -28,7 +28,8 @@ EXPORTS = ("moe_workspace_size", "moe_status_str", "moe_tile_experts", "moe_rout
            "moe_grouped_ffn", "moe_ffn_gate_up", "moe_ffn_down", "moe_ffn_fused",
            "moe_ffn_fused_items", "moe_device_clock_khz", "moe_combine", "moe_layer",
            "moe_stage_experts", "moe_route_locality_blocks", "moe_route_locality",
-           "moe_stream_read", "moe_layer_noalloc")
+           "moe_stream_read", "moe_layer_noalloc", "moe_route_permute",
+           "moe_ffn_down_combine")
 MOE_F_TILED_WEIGHTS = 0x1
 MOE_F_CHECK_FINITE = 0x2
 MOE_F_FUSED_FFN = 0x4
@@ -99,9 +100,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                               P(moe_perm), vp, sz, vp]
     lib.moe_layer_noalloc.argtypes = [P(moe_shape), vp, vp, vp, P(moe_experts), vp, vp, vp, vp,
                                       P(moe_perm), vp]
+    lib.moe_route_permute.argtypes = [P(moe_shape), vp, vp, vp, vp, vp, vp, P(moe_perm), vp, sz, vp]
+    lib.moe_ffn_down_combine.argtypes = [P(moe_shape), vp, P(moe_experts), P(moe_perm), vp, vp, vp,
+                                         vp, sz, vp]
     for name in ("moe_tile_experts", "moe_route", "moe_permute", "moe_grouped_ffn", "moe_ffn_gate_up",
                  "moe_ffn_down", "moe_ffn_fused", "moe_device_clock_khz", "moe_combine", "moe_layer",
-                 "moe_route_locality", "moe_stage_experts", "moe_stream_read", "moe_layer_noalloc"):
+                 "moe_route_locality", "moe_stage_experts", "moe_stream_read", "moe_layer_noalloc", "moe_route_permute",
+                 "moe_ffn_down_combine"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -171,6 +176,25 @@ def moe_permute(shape, topk_ids, perm, workspace=None, workspace_bytes=0, stream
                             None if perm is None else ctypes.byref(perm), ptr(workspace),
                             workspace_bytes, stream_handle(stream))
     return _ret(st, "moe_permute", check)
+
+
+def moe_route_permute(shape, x, w_router, router_bias, topk_ids, topk_w, logits, perm, workspace,
+                      workspace_bytes, stream=None, check=True) -> int:
+    st = load().moe_route_permute(ctypes.byref(shape), ptr(x), ptr(w_router), ptr(router_bias),
+                                  ptr(topk_ids), ptr(topk_w), ptr(logits),
+                                  None if perm is None else ctypes.byref(perm), ptr(workspace),
+                                  workspace_bytes, stream_handle(stream))
+    return _ret(st, "moe_route_permute", check)
+
+
+def moe_ffn_down_combine(shape, h, experts, perm, topk_w, residual, out, workspace, workspace_bytes,
+                         stream=None, check=True) -> int:
+    st = load().moe_ffn_down_combine(ctypes.byref(shape), ptr(h),
+                                     None if experts is None else ctypes.byref(experts),
+                                     None if perm is None else ctypes.byref(perm), ptr(topk_w),
+                                     ptr(residual), ptr(out), ptr(workspace), workspace_bytes,
+                                     stream_handle(stream))
+    return _ret(st, "moe_ffn_down_combine", check)
 
 
 def moe_grouped_ffn(shape, x, experts, perm, y, workspace, workspace_bytes, stream=None,

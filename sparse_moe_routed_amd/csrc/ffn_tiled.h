@@ -112,9 +112,11 @@ template <int NB, int MB>
 constexpr int out_tile_bytes() {
   return 16 * NB * (128 * MB + 16);
 }
-template <int NB, int MB, typename Val>
-__device__ __forceinline__ void store_tile(char* lds, Val&& val, int rows,
-                                           uint16_t* __restrict__ dst, size_t ld, int col0) {
+// With a store functor: store(row, col, v) writes the 16 bytes v of tile row
+// `row` at column `col` (8 values) wherever the caller keeps them.
+template <int NB, int MB, typename Val, typename Store>
+__device__ __forceinline__ void store_tile_rows(char* lds, Val&& val, int rows, Store store,
+                                                int col0) {
   constexpr int pitch = 128 * MB + 16;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
@@ -135,9 +137,19 @@ __device__ __forceinline__ void store_tile(char* lds, Val&& val, int rows,
     const int g = it * 256 + static_cast<int>(threadIdx.x);
     const int row = g / segs, cs = g % segs;
     if (g < total && row < rows)
-      *reinterpret_cast<u32x4_t*>(dst + static_cast<size_t>(row) * ld + col0 + cs * 8) =
-          *reinterpret_cast<const u32x4_t*>(lds + row * pitch + cs * 16);
+      store(row, col0 + cs * 8, *reinterpret_cast<const u32x4_t*>(lds + row * pitch + cs * 16));
   }
+}
+
+template <int NB, int MB, typename Val>
+__device__ __forceinline__ void store_tile(char* lds, Val&& val, int rows,
+                                           uint16_t* __restrict__ dst, size_t ld, int col0) {
+  store_tile_rows<NB, MB>(
+      lds, val, rows,
+      [&](int row, int col, u32x4_t v) {
+        *reinterpret_cast<u32x4_t*>(dst + static_cast<size_t>(row) * ld + col) = v;
+      },
+      col0);
 }
 
 // ---------------------------------------------------------------------------
@@ -146,9 +158,28 @@ __device__ __forceinline__ void store_tile(char* lds, Val&& val, int rows,
 // four consecutive 1 KB fragments), 16 B (int4) or 8 B (int2), plus 8 B of
 // scales, so every load instruction of a wave reads one contiguous block.
 // ---------------------------------------------------------------------------
+// Raw weight bits of one 16-row block and k unit held by a lane: bf16 four
+// 16-byte fragments, int4 16 bytes, int2 8 bytes.
 template <int WF>
 struct TRaw {
-  u32x4_t v[WF == WF_BF16 ? 4 : 1];
+  u32x4_t v[4];
+};
+template <>
+struct TRaw<WF_INT4> {
+  u32x4_t v[1];
+};
+template <>
+struct TRaw<WF_INT2> {
+  u32x2_t v[1];
+};
+
+// The four fp16 group scales (k chunks 0..3 of a unit) of one weight row,
+// kept packed in two registers.
+struct TScales {
+  u32x2_t v;
+  __device__ __forceinline__ float f32(int st) const {
+    return fp16_to_f32(static_cast<uint16_t>(v[st >> 1] >> (16 * (st & 1))));
+  }
 };
 
 // Cache policy of the weight loads (the aux operand of the raw buffer loads).
@@ -206,9 +237,8 @@ __device__ __forceinline__ TRaw<WF> tload(const Slab<WF>& S, int mb, int kb, int
     t.v[0] = __builtin_amdgcn_raw_buffer_load_b128(S.w, lane * 16, (mb * (S.K / 128) + kb) * 1024,
                                                    AUX);
   } else {
-    const u32x2_t d =
+    t.v[0] =
         __builtin_amdgcn_raw_buffer_load_b64(S.w, lane * 8, (mb * (S.K / 128) + kb) * 512, AUX);
-    t.v[0] = u32x4_t{d[0], d[1], 0u, 0u};
   }
   return t;
 }
@@ -241,15 +271,9 @@ __device__ __forceinline__ u32x4_t tdecode(const TRaw<WF>& t, int s, Dq d) {
 
 // fp16 scales of groups 4 kb .. 4 kb + 3 of row r of block mb.
 template <int WF, int AUX>
-__device__ __forceinline__ Scales<4> tscales(const Slab<WF>& S, int mb, int kb, int r) {
-  const u32x2_t v =
-      __builtin_amdgcn_raw_buffer_load_b64(S.s, r * 8, (mb * (S.K / 128) + kb) * 128, AUX);
-  Scales<4> o;
-  o.s[0] = static_cast<uint16_t>(v[0]);
-  o.s[1] = static_cast<uint16_t>(v[0] >> 16);
-  o.s[2] = static_cast<uint16_t>(v[1]);
-  o.s[3] = static_cast<uint16_t>(v[1] >> 16);
-  return o;
+__device__ __forceinline__ TScales tscales(const Slab<WF>& S, int mb, int kb, int r) {
+  return TScales{
+      __builtin_amdgcn_raw_buffer_load_b64(S.s, r * 8, (mb * (S.K / 128) + kb) * 128, AUX)};
 }
 
 template <int WF>

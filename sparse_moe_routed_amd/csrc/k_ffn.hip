@@ -359,7 +359,7 @@ __global__ __launch_bounds__(256) void k_gateup_t(
       for (int b = 0; b < NB; ++b) acc[mb][gu][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   struct Stage {
-    Scales<4> sc[MB][2];
+    TScales sc[MB][2];
     TRaw<WF> raw[MB][2];
     u32x4_t xa[4][NB];
   };
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256) void k_gateup_t(
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[mb][gu][b] = mfma_bf16(S.xa[st][b], wv, acc[mb][gu][b]);
           } else {
-            const float sv = fp16_to_f32(S.sc[mb][gu].s[st]);
+            const float sv = S.sc[mb][gu].f32(st);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
               const f32x4_t pp = mfma_bf16(S.xa[st][b], wv, corr[b]);
@@ -463,14 +463,17 @@ __global__ __launch_bounds__(256) void k_gateup_t(
 // SH: the tile's intermediate rows [16 NB][I] are copied into LDS once (rows
 // of 2 I + 16 bytes, dynamic LDS) and the four waves read their fragments
 // there, instead of each wave gathering the same rows from L2 for every k
-// unit.
-template <int WF, int NB, int MB, bool PF, bool SH>
+// unit.  PAIRY: row r of the tile is stored at y[sorted_pair[row0 + r]] (its
+// pair slot) instead of y[row0 + r], so the combine reads a token's slots
+// without the pair -> row indirection.
+template <int WF, int NB, int MB, bool PF, bool SH, bool PAIRY>
 __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
                                                 const uint8_t* __restrict__ wd,
                                                 const uint16_t* __restrict__ sd,
                                                 const int32_t* __restrict__ tiles, int max_tiles,
                                                 int H, int I, uint16_t* __restrict__ y,
-                                                int band, int xcd) {
+                                                int band, int xcd,
+                                                const int32_t* __restrict__ sorted_pair, int P) {
   // the output tile goes through LDS when a wave owns 2+ row blocks (int4
   // stack step -1.2%); with one (bf16 decode) direct stores measured 0.3%
   // faster
@@ -481,6 +484,19 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
   if (!tile_item(tiles[3 * max_tiles], H / (64 * MB), band, xcd != 0, ti, sl)) return;
   const Tile tl = read_tile(tiles, ti);
   if (tl.rows <= 0) return;
+  // the output row of tile row rr
+  auto out_row = [&](int rr) -> size_t {
+    if constexpr (PAIRY) return static_cast<size_t>(min(max(sorted_pair[tl.row0 + rr], 0), P - 1));
+    else return static_cast<size_t>(tl.row0 + rr);
+  };
+  size_t orow[NB][4];   // direct stores: the rows this lane writes (16 b + 4 q + j)
+  if constexpr (!kStageOut) {
+    const int q4 = (threadIdx.x & 63) >> 4;
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) orow[b][j] = out_row(min(b * 16 + 4 * q4 + j, tl.rows - 1));
+  }
   const int hp = 2 * I + 16;   // SH: LDS row pitch in bytes (rows 16 bytes = 4 banks apart)
   if constexpr (SH) {
     // 16-byte chunks; rows past the tile repeat its last row (never stored)
@@ -525,7 +541,7 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
     for (int b = 0; b < NB; ++b) acc[mb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   struct Stage {
-    Scales<4> sc[MB];
+    TScales sc[MB];
     TRaw<WF> raw[MB];
     u32x4_t ha[SH ? 1 : 4][NB];
     int u;
@@ -571,7 +587,7 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
 #pragma unroll
           for (int b = 0; b < NB; ++b) acc[mb][b] = mfma_bf16(ha[b], wv, acc[mb][b]);
         } else {
-          const float sv = fp16_to_f32(S.sc[mb].s[st]);
+          const float sv = S.sc[mb].f32(st);
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
             const f32x4_t pp = mfma_bf16(ha[b], wv, corr[b]);
@@ -584,8 +600,11 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
   };
   unit_loop<PF, Stage>(0, I / 128, load, compute);
   if constexpr (kStageOut) {
-    store_tile<NB, MB>(ot, [&](int mb, int b, int j) { return acc[mb][b][j]; }, tl.rows,
-                       y + static_cast<size_t>(tl.row0) * H, H, sl * 64 * MB);
+    store_tile_rows<NB, MB>(ot, [&](int mb, int b, int j) { return acc[mb][b][j]; }, tl.rows,
+                            [&](int row, int col, u32x4_t v) {
+                              *reinterpret_cast<u32x4_t*>(y + out_row(row) * H + col) = v;
+                            },
+                            sl * 64 * MB);
   } else {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -595,8 +614,7 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int rr = b * 16 + 4 * q + j;
-          if (rr < tl.rows)
-            y[static_cast<size_t>(tl.row0 + rr) * H + n] = f32_to_bf16(acc[mb][b][j]);
+          if (rr < tl.rows) y[orow[b][j] * H + n] = f32_to_bf16(acc[mb][b][j]);
         }
     }
   }
@@ -706,7 +724,7 @@ __device__ __forceinline__ void gateup_x_body(
       for (int b = 0; b < NB; ++b) acc[mb][gu][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   struct Stage {
-    Scales<4> sc[MB][2];
+    TScales sc[MB][2];
     TRaw<WF> raw[MB][2];
   };
   // bf16: group f = fragment f (k chunk f) of every block; low-bit: one
@@ -762,7 +780,7 @@ __device__ __forceinline__ void gateup_x_body(
 #pragma unroll
         for (int gu = 0; gu < 2; ++gu) {
           const u32x4_t wv = tdecode<WF>(w.raw[mb][gu], st, dq);
-          const float sv = fp16_to_f32(w.sc[mb][gu].s[st]);
+          const float sv = w.sc[mb][gu].f32(st);
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
             const f32x4_t pp = mfma_bf16(xa[b], wv, corr[b]);
@@ -824,7 +842,7 @@ __device__ __forceinline__ void down_x_body(const uint16_t* __restrict__ h,
     for (int b = 0; b < NB; ++b) acc[mb][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   struct Stage {
-    Scales<4> sc[MB];
+    TScales sc[MB];
     TRaw<WF> raw[MB];
   };
   constexpr int NF = WF == WF_BF16 ? 4 : 1;
@@ -859,7 +877,7 @@ __device__ __forceinline__ void down_x_body(const uint16_t* __restrict__ h,
 #pragma unroll
           for (int b = 0; b < NB; ++b) acc[mb][b] = mfma_bf16(ha[b], wv, acc[mb][b]);
         } else {
-          const float sv = fp16_to_f32(w.sc[mb].s[st]);
+          const float sv = w.sc[mb].f32(st);
 #pragma unroll
           for (int b = 0; b < NB; ++b) {
             const f32x4_t pp = mfma_bf16(ha[b], wv, corr[b]);
@@ -1124,7 +1142,7 @@ static void gateup_nb(const moe_shape& s, const Plan& pl, const void* x, const m
 template <int WF, int NB, int MB>
 static void down_tiled_launch(const moe_shape& s, const Plan& pl, const void* h,
                               const moe_experts& ex, const int32_t* tiles, void* y,
-                              hipStream_t st) {
+                              const int32_t* pairy, hipStream_t st) {
   const TileOrder o = tile_order(pl, false);
   if constexpr (NB >= 4) {
     // 128-row plan tiles run as two 64-row halves (measured: the 128-row down
@@ -1140,41 +1158,44 @@ static void down_tiled_launch(const moe_shape& s, const Plan& pl, const void* h,
     // low-bit single-block tiles stage their intermediate rows in LDS
     const size_t lds = static_cast<size_t>(16 * NB) * (2 * s.I + 16);
     const bool sh = WF != WF_BF16 && NB == 1 && lds <= 64 * 1024;
-    auto kern = sh ? k_down_t<WF, NB, MB, tile_pf<WF, NB>(), true>
-                   : k_down_t<WF, NB, MB, tile_pf<WF, NB>(), false>;
+    auto kern = pairy ? (sh ? k_down_t<WF, NB, MB, tile_pf<WF, NB>(), true, true>
+                            : k_down_t<WF, NB, MB, tile_pf<WF, NB>(), false, true>)
+                      : (sh ? k_down_t<WF, NB, MB, tile_pf<WF, NB>(), true, false>
+                            : k_down_t<WF, NB, MB, tile_pf<WF, NB>(), false, false>);
     hipLaunchKernelGGL(kern, item_grid(pl, s.H / (64 * MB)), dim3(256), sh ? lds : 0, st,
                        static_cast<const uint16_t*>(h), static_cast<const uint8_t*>(ex.down),
                        ex.down_scale, tiles, pl.max_tiles, s.H, s.I, static_cast<uint16_t*>(y),
-                       min(o.band, pl.max_tiles), o.xcd);
+                       min(o.band, pl.max_tiles), o.xcd, pairy, s.T * s.top_k);
   }
 }
 
 template <int WF, int NB>
 static void launch_down_tiled(const moe_shape& s, const Plan& pl, const void* h,
                               const moe_experts& ex, const int32_t* tiles, void* y,
-                              hipStream_t st) {
+                              const int32_t* pairy, hipStream_t st) {
   constexpr int M = tile_mb_max<WF, NB, false>();
   switch (tiled_mb<WF, NB>(s.H, 64, M)) {
-    case M: down_tiled_launch<WF, NB, M>(s, pl, h, ex, tiles, y, st); break;
-    case (M > 1 ? M / 2 : 0): down_tiled_launch<WF, NB, (M > 1 ? M / 2 : 1)>(s, pl, h, ex, tiles, y, st); break;
-    default: down_tiled_launch<WF, NB, 1>(s, pl, h, ex, tiles, y, st); break;
+    case M: down_tiled_launch<WF, NB, M>(s, pl, h, ex, tiles, y, pairy, st); break;
+    case (M > 1 ? M / 2 : 0):
+      down_tiled_launch<WF, NB, (M > 1 ? M / 2 : 1)>(s, pl, h, ex, tiles, y, pairy, st); break;
+    default: down_tiled_launch<WF, NB, 1>(s, pl, h, ex, tiles, y, pairy, st); break;
   }
 }
 
 template <int WF>
 static void down_nb(const moe_shape& s, const Plan& pl, const void* h, const moe_experts& ex,
-                    const int32_t* tiles, void* y, hipStream_t st) {
+                    const int32_t* tiles, void* y, hipStream_t st, const int32_t* pairy = nullptr) {
   if constexpr (WF == WF_BF16) {
     if (pl.nb == 8) {   // bf16 tiled only (plan_nb): 64-row halves of the 128-row tiles
-      launch_down_tiled<WF, 4>(s, pl, h, ex, tiles, y, st);
+      launch_down_tiled<WF, 4>(s, pl, h, ex, tiles, y, nullptr, st);
       return;
     }
   }
   if (s.flags & MOE_F_TILED_WEIGHTS) {
     switch (pl.nb) {
-      case 1: launch_down_tiled<WF, 1>(s, pl, h, ex, tiles, y, st); break;
-      case 2: launch_down_tiled<WF, 2>(s, pl, h, ex, tiles, y, st); break;
-      default: launch_down_tiled<WF, 4>(s, pl, h, ex, tiles, y, st); break;
+      case 1: launch_down_tiled<WF, 1>(s, pl, h, ex, tiles, y, pairy, st); break;
+      case 2: launch_down_tiled<WF, 2>(s, pl, h, ex, tiles, y, nullptr, st); break;
+      default: launch_down_tiled<WF, 4>(s, pl, h, ex, tiles, y, nullptr, st); break;
     }
     return;
   }
@@ -1218,6 +1239,32 @@ hipError_t launch_down(const moe_shape& s, const Plan& pl, const void* h, const 
     down_nb<WF_INT2>(s, pl, h, ex, tiles, y, st);
   }
   return hipGetLastError();
+}
+
+// Down followed by the combine.  With 16-row tiles of tiled bf16-activation
+// weights the down kernel writes each y row to its pair slot and the
+// combine reads a token's k slots directly (one memory round trip instead
+// of two); otherwise y in permuted row order and the combine through
+// pair_row.
+bool down_pair_order(const moe_shape& s, const Plan& pl) {
+  return s.act == MOE_DT_BF16 && (s.flags & MOE_F_TILED_WEIGHTS) && pl.nb == 1;
+}
+
+hipError_t launch_down_combine(const moe_shape& s, const Plan& pl, const void* h,
+                               const moe_experts& ex, const int32_t* tiles,
+                               const int32_t* sorted_pair, const int32_t* pair_row, const float* w,
+                               const void* residual, void* out, void* y, hipStream_t st) {
+  if (!down_pair_order(s, pl)) {
+    hipError_t e = launch_down(s, pl, h, ex, tiles, y, st);
+    if (e == hipSuccess) e = launch_combine(s, y, pair_row, w, residual, out, st);
+    return e;
+  }
+  if (s.wfmt == MOE_WF_DENSE) down_nb<WF_BF16>(s, pl, h, ex, tiles, y, st, sorted_pair);
+  else if (s.wfmt == MOE_WF_INT4_G32) down_nb<WF_INT4>(s, pl, h, ex, tiles, y, st, sorted_pair);
+  else down_nb<WF_INT2>(s, pl, h, ex, tiles, y, st, sorted_pair);
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = launch_combine(s, y, nullptr, w, residual, out, st);
+  return e;
 }
 
 hipError_t launch_ffn(const moe_shape& s, const Plan& pl, const void* x, const moe_experts& ex,

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(256) void k_ffn_fused(
 
   const int units = H / 128;
   for (int u0 = 0; u0 < units; u0 += US) {
-    Scales<4> sc[US][2];
+    TScales sc[US][2];
     TRaw<WF> raw[US][2];
     u32x4_t xa[US][4][NB];
 #pragma unroll
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(256) void k_ffn_fused(
 #pragma unroll
             for (int b = 0; b < NB; ++b) acc[gu][b] = mfma_bf16(xa[v][st][b], wv, acc[gu][b]);
           } else {
-            const float sv = fp16_to_f32(sc[v][gu].s[st]);
+            const float sv = sc[v][gu].f32(st);
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
               const f32x4_t pp = mfma_bf16(xa[v][st][b], wv, corr[b]);

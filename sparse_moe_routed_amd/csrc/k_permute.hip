@@ -15,6 +15,7 @@
 // each chunk its base row per expert, then a per-chunk bitmap placement).
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "perm_device.h"
 
 namespace moe {
 
@@ -109,8 +110,8 @@ __device__ void permute_small_body(const int32_t* ids, int T, int k, int E, int 
                                    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_row,
                                    int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                                    int rt, int max_tiles, int32_t* __restrict__ tiles,
-                                   uint32_t* bits, uint32_t* pre, int* s_cnt, int* s_off,
-                                   int* s_act, int* s_tot) {
+                                   uint32_t* bits, uint32_t* pre, int* s_cnt,
+                                   int* s_off, int* s_act, int* s_tot) {
   const int tid = threadIdx.x;
   const int P = T * k;
 
@@ -137,7 +138,6 @@ __device__ void permute_small_body(const int32_t* ids, int T, int k, int E, int 
   if (tid == 0) n_active[0] = nact;
   __syncthreads();
   if (tiles != nullptr) emit_tiles(nact, s_act, s_cnt, s_off, P, rt, max_tiles, tiles, s_tot);
-
   for (int p = tid; p < P; p += blockDim.x) {
     const int e = ids[p];
     if (e < 0 || e >= E) continue;
@@ -164,107 +164,17 @@ __global__ __launch_bounds__(1024) void k_permute_small(
                      max_tiles, tiles, dyn, dyn + E * W, s_cnt, s_off, s_act, s_tot);
 }
 
-// Up to 32 tokens (one bitmap word per expert; decode and verifier blocks),
-// E <= 1024: 256 threads, each owning up to 4 consecutive experts, one
-// combined scan of (rows, active flag, tiles) per expert in expert order, 4
-// barriers.  Same outputs as permute_small_body (the stable counting sort,
-// active experts ascending, tiles in active order).
+// Up to 32 tokens: permute_w1_body (perm_device.h) in one 256-thread
+// workgroup, 4 barriers (against 13 barriers of 16 waves in the general
+// single-workgroup kernel).
 __global__ __launch_bounds__(256) void k_permute_w1(
     const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
     int32_t* __restrict__ pair_row, int32_t* __restrict__ active, int32_t* __restrict__ n_active,
     int rt, int max_tiles, int32_t* __restrict__ tiles) {
-  __shared__ uint32_t bits[1024];
-  __shared__ int s_off[1024];
-  __shared__ int wtot[4][3];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int P = T * k;
-  const int ept = (E + 255) / 256;   // experts per thread (<= 4)
-  const int e0 = tid * ept;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (i < ept && e0 + i < E) bits[e0 + i] = 0u;
-  __syncthreads();
-  for (int p = tid; p < P; p += 256) {
-    const int e = ids[p];
-    if (e >= 0 && e < E) atomicOr(&bits[e], 1u << (p / k));
-  }
-  __syncthreads();
-  int c[4], n[4], C = 0, F = 0, N = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    c[i] = (i < ept && e0 + i < E) ? __popc(bits[e0 + i]) : 0;
-    n[i] = (c[i] + rt - 1) / rt;
-    C += c[i];
-    F += c[i] > 0 ? 1 : 0;
-    N += n[i];
-  }
-  // inclusive wave scans of the three per-thread sums, then wave offsets
-  int iC = C, iF = F, iN = N;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int a = __shfl_up(iC, off, kWave), b = __shfl_up(iF, off, kWave),
-              d = __shfl_up(iN, off, kWave);
-    if (lane >= off) {
-      iC += a;
-      iF += b;
-      iN += d;
-    }
-  }
-  if (lane == 63) {
-    wtot[wave][0] = iC;
-    wtot[wave][1] = iF;
-    wtot[wave][2] = iN;
-  }
-  __syncthreads();
-  int bC = 0, bF = 0, bN = 0, tF = 0, tN = 0;   // this wave's base; totals
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (w < wave) {
-      bC += wtot[w][0];
-      bF += wtot[w][1];
-      bN += wtot[w][2];
-    }
-    tF += wtot[w][1];
-    tN += wtot[w][2];
-  }
-  int off = bC + iC - C, apos = bF + iF - F, tpos = bN + iN - N;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int e = e0 + i;
-    if (i >= ept || e >= E) break;
-    counts[e] = c[i];
-    offsets[e] = off;
-    s_off[e] = off;
-    if (e == E - 1) offsets[E] = off + c[i];
-    if (c[i] > 0) active[apos++] = e;
-    if (e >= tF) active[e] = -1;
-    if (tiles != nullptr) {
-      for (int j = 0; j < n[i]; ++j) {
-        const int ti = tpos + j;
-        if (ti >= max_tiles) break;
-        const int r0 = off + j * rt;
-        tiles[3 * ti] = e;
-        tiles[3 * ti + 1] = r0;
-        tiles[3 * ti + 2] = min(min(rt, c[i] - j * rt), P - r0);
-      }
-    }
-    off += c[i];
-    tpos += n[i];
-  }
-  if (tid == 0) {
-    n_active[0] = tF;
-    if (tiles != nullptr) tiles[3 * max_tiles] = min(tN, max_tiles);
-  }
-  __syncthreads();
-  for (int p = tid; p < P; p += 256) {
-    const int e = ids[p];
-    if (e < 0 || e >= E) continue;
-    const int t = p / k;
-    const int row = s_off[e] + __popc(bits[e] & ((1u << t) - 1u));
-    sorted_pair[row] = p;
-    pair_row[p] = row;
-  }
+  __shared__ PermW1Lds lds;
+  permute_w1_body(ids, T, k, E, counts, offsets, sorted_pair, pair_row, active, n_active, rt,
+                  max_tiles, tiles, lds);
 }
 
 // Large batches: chunks of kChunkTok tokens.
@@ -406,7 +316,7 @@ __global__ __launch_bounds__(1024) void k_plan_tiles(const int32_t* __restrict__
 hipError_t launch_permute(const moe_shape& s, const Plan& pl, const int32_t* ids,
                           const PermPtrs& pp, int32_t* tiles, void* ws, hipStream_t st) {
   const int rt = 16 * pl.nb;
-  if (s.T <= 32 && s.E <= 1024) {
+  if (permute_w1_ok(s)) {
     hipLaunchKernelGGL(k_permute_w1, dim3(1), dim3(256), 0, st, ids, s.T, s.top_k, s.E,
                        pp.counts, pp.offsets, pp.sorted_pair, pp.pair_row, pp.active,
                        pp.n_active, rt, pl.max_tiles, tiles);

@@ -11,6 +11,7 @@
 
 #include "moe_device.h"
 #include "moe_internal.h"
+#include "perm_device.h"
 #include "route_device.h"
 
 namespace moe {
@@ -29,12 +30,16 @@ namespace moe {
 // Small batches: one workgroup per (16-token x 16-expert tile, group of
 // parts), one wave per part; the group's part sums are added through LDS and
 // stored in float64 to gsum[group][T][E] (the top-k kernel finishes the
-// logits).  grid (ceil(T/16), ceil(E/16), ngroups), block 64 * kRouterGroup.
+// logits).  `arrive` (route + permute in one call): the top-k kernel's
+// arrival counter, zeroed here.  grid (ceil(T/16), ceil(E/16), ngroups),
+// block 64 * kRouterGroup.
 __global__ __launch_bounds__(64 * kRouterGroup) void k_router_parts(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int H, int E,
-    int nparts, double* __restrict__ gsum) {
+    int nparts, double* __restrict__ gsum, int32_t* __restrict__ arrive) {
   __shared__ double red[kRouterGroup][64][4];
   const int wave = threadIdx.x >> 6;
+  if (arrive != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0)
+    *arrive = 0;
   const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16, g = blockIdx.z;
   const int p0 = g * kRouterGroup, np = min(kRouterGroup, nparts - p0);
   if (wave < np) router_part(x, wr, T, H, E, nparts, t0, e0, p0 + wave, red[wave]);
@@ -194,21 +199,34 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ logits, 
   topk_select<NV>(v, E, k, sel[wave], ids + o, w + o);
 }
 
+// Permutation outputs of the fused route + permute launch.
+struct PermArgs {
+  PermPtrs pp;
+  int rt, max_tiles;
+  int32_t* tiles;
+  int32_t* arrive;   // zeroed by the router kernel of the same call
+};
+
 // Small bf16 batches: finish the logits of one token from the router's
 // group sums, then its exact top-k.  Workgroup per token; wave w finishes
 // the experts of slots w, w+4, ... (the ngroups float64 group sums, all
 // loaded before any is added, summed in group order, bias added, rounded
 // once to float32) into LDS and `logits`; after a barrier wave 0 selects.
-// grid T, block 256.
-template <int NV>
+// PERM (up to 32 tokens): every workgroup then publishes its token's routes
+// (device-coherent stores, arrival counter); the last one to arrive reads
+// them all and builds the permutation and the tile plan (permute_w1_body),
+// so routing and grouping take one launch.  grid T, block 256.
+template <int NV, bool PERM>
 __global__ __launch_bounds__(256) void k_topk_groups(const double* __restrict__ gsum, int ngroups,
                                                      const float* __restrict__ bias,
                                                      float* __restrict__ logits, int T, int E, int k,
                                                      int32_t* __restrict__ ids,
-                                                     float* __restrict__ w) {
+                                                     float* __restrict__ w, PermArgs pa) {
   constexpr int NJ = (NV + 3) / 4;   // slots per wave
   __shared__ float lv[NV * 64];
   __shared__ float sel[1024];
+  __shared__ PermW1Lds plds;   // PERM only (unused LDS is not allocated)
+  __shared__ int s_last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int t = blockIdx.x;
   const size_t slice = static_cast<size_t>(T) * E;
@@ -236,20 +254,38 @@ __global__ __launch_bounds__(256) void k_topk_groups(const double* __restrict__ 
     if (j * 64 + lane < E) logits[static_cast<size_t>(t) * E + j * 64 + lane] = f;
   }
   __syncthreads();
-  if (wave != 0) return;
-  float v[NV];
+  if (wave == 0) {
+    float v[NV];
 #pragma unroll
-  for (int j = 0; j < NV; ++j) v[j] = lv[j * 64 + lane];
-  const size_t o = static_cast<size_t>(t) * k;
-  topk_select<NV>(v, E, k, sel, ids + o, w + o);
+    for (int j = 0; j < NV; ++j) v[j] = lv[j * 64 + lane];
+    const size_t o = static_cast<size_t>(t) * k;
+    topk_select<NV, PERM>(v, E, k, sel, ids + o, w + o);
+  }
+  if constexpr (PERM) {
+    // the ids went out device-coherent (no device-scope fence: it would
+    // write back and invalidate the XCD's whole L2); wait for them, count
+    // this token done, and let the last token's workgroup group the pairs
+    wait_memory_done();
+    __syncthreads();
+    if (threadIdx.x == 0) s_last = atomicAdd(pa.arrive, 1) == T - 1;
+    __syncthreads();
+    if (!s_last) return;
+    permute_w1_body<true>(ids, T, k, E, pa.pp.counts, pa.pp.offsets, pa.pp.sorted_pair,
+                          pa.pp.pair_row, pa.pp.active, pa.pp.n_active, pa.rt, pa.max_tiles,
+                          pa.tiles, plds);
+    if (threadIdx.x == 0) store_dev_i32(pa.arrive, 0);
+  }
 }
 
 template <int NV>
 static void launch_topk(const moe_shape& s, const double* gsum, int ngroups, const float* bias,
-                        float* lg, int32_t* ids, float* w, hipStream_t st) {
-  if (gsum)
-    hipLaunchKernelGGL((k_topk_groups<NV>), dim3(s.T), dim3(256), 0, st, gsum, ngroups, bias, lg,
-                       s.T, s.E, s.top_k, ids, w);
+                        float* lg, int32_t* ids, float* w, const PermArgs* pa, hipStream_t st) {
+  if (gsum && pa)
+    hipLaunchKernelGGL((k_topk_groups<NV, true>), dim3(s.T), dim3(256), 0, st, gsum, ngroups, bias,
+                       lg, s.T, s.E, s.top_k, ids, w, *pa);
+  else if (gsum)
+    hipLaunchKernelGGL((k_topk_groups<NV, false>), dim3(s.T), dim3(256), 0, st, gsum, ngroups, bias,
+                       lg, s.T, s.E, s.top_k, ids, w, PermArgs{});
   else
     hipLaunchKernelGGL((k_topk<NV>), dim3((s.T + 3) / 4), dim3(256), 0, st, lg, s.T, s.E, s.top_k,
                        ids, w);
@@ -258,7 +294,8 @@ static void launch_topk(const moe_shape& s, const double* gsum, int ngroups, con
 // The router logits, or (bf16 batches up to 1024 tokens) their group sums
 // in `gsum`.
 static hipError_t launch_router(const moe_shape& s, const void* x, const void* w_router,
-                                const float* bias, float* lg, double* gsum, hipStream_t st) {
+                                const float* bias, float* lg, double* gsum, int32_t* arrive,
+                                hipStream_t st) {
   if (s.act == MOE_DT_BF16) {
     const int np = router_parts(s.H);
     const unsigned ng = gsum ? static_cast<unsigned>(router_groups(s.H)) : 1u;
@@ -267,7 +304,7 @@ static hipError_t launch_router(const moe_shape& s, const void* x, const void* w
     if (s.T <= 64) {
       dim3 grid((s.T + 15) / 16, (s.E + 15) / 16, ng);
       hipLaunchKernelGGL(k_router_parts, grid, dim3(64 * kRouterGroup), 0, st, xb, wb, s.T, s.H,
-                         s.E, np, gsum);
+                         s.E, np, gsum, arrive);
     } else if (s.T <= 1024) {
       dim3 grid((s.T + 31) / 32, (s.E + 31) / 32, ng);
       auto kern = gsum ? k_router_lds<1, true> : k_router_lds<1, false>;
@@ -286,22 +323,57 @@ static hipError_t launch_router(const moe_shape& s, const void* x, const void* w
   return hipGetLastError();
 }
 
-hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const void* w_router,
-                        const float* bias, int32_t* ids, float* w, float* logits, void* ws,
-                        hipStream_t st) {
+// The routing of one call; with `pp` (route + permute in one launch) the
+// permutation and tile plan too.
+static hipError_t route_impl(const moe_shape& s, const Plan& pl, const void* x,
+                             const void* w_router, const float* bias, int32_t* ids, float* w,
+                             float* logits, void* ws, const PermPtrs* pp, int32_t* tiles,
+                             hipStream_t st) {
   float* lg = logits ? logits : reinterpret_cast<float*>(static_cast<char*>(ws) + pl.logits_off);
   double* gsum = router_gsum(s) ? reinterpret_cast<double*>(static_cast<char*>(ws) + pl.gsum_off)
                                 : nullptr;
-  hipError_t e = launch_router(s, x, w_router, bias, lg, gsum, st);
+  PermArgs pa{};
+  const PermArgs* pap = nullptr;
+  if (pp) {
+    pa.pp = *pp;
+    pa.rt = 16 * pl.nb;
+    pa.max_tiles = pl.max_tiles;
+    pa.tiles = tiles;
+    pa.arrive = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + pl.tiles_off) +
+                3 * pl.max_tiles + 1;
+    pap = &pa;
+  }
+  hipError_t e = launch_router(s, x, w_router, bias, lg, gsum, pap ? pa.arrive : nullptr, st);
   if (e != hipSuccess) return e;
   const int nv = (s.E + 63) / 64, ng = router_groups(s.H);
   const float* fb = gsum ? bias : nullptr;   // the other paths added the bias already
-  if (nv <= 1) launch_topk<1>(s, gsum, ng, fb, lg, ids, w, st);
-  else if (nv <= 2) launch_topk<2>(s, gsum, ng, fb, lg, ids, w, st);
-  else if (nv <= 4) launch_topk<4>(s, gsum, ng, fb, lg, ids, w, st);
-  else if (nv <= 8) launch_topk<8>(s, gsum, ng, fb, lg, ids, w, st);
-  else launch_topk<16>(s, gsum, ng, fb, lg, ids, w, st);
+  if (nv <= 1) launch_topk<1>(s, gsum, ng, fb, lg, ids, w, pap, st);
+  else if (nv <= 2) launch_topk<2>(s, gsum, ng, fb, lg, ids, w, pap, st);
+  else if (nv <= 4) launch_topk<4>(s, gsum, ng, fb, lg, ids, w, pap, st);
+  else if (nv <= 8) launch_topk<8>(s, gsum, ng, fb, lg, ids, w, pap, st);
+  else launch_topk<16>(s, gsum, ng, fb, lg, ids, w, pap, st);
   return hipGetLastError();
+}
+
+hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const void* w_router,
+                        const float* bias, int32_t* ids, float* w, float* logits, void* ws,
+                        hipStream_t st) {
+  return route_impl(s, pl, x, w_router, bias, ids, w, logits, ws, nullptr, nullptr, st);
+}
+
+bool route_permute_fused(const moe_shape& s) {
+  return s.act == MOE_DT_BF16 && router_gsum(s) && s.T <= 64 && permute_w1_ok(s);
+}
+
+hipError_t launch_route_permute(const moe_shape& s, const Plan& pl, const void* x,
+                                const void* w_router, const float* bias, int32_t* ids, float* w,
+                                float* logits, const PermPtrs& pp, int32_t* tiles, void* ws,
+                                hipStream_t st) {
+  if (route_permute_fused(s))
+    return route_impl(s, pl, x, w_router, bias, ids, w, logits, ws, &pp, tiles, st);
+  hipError_t e = route_impl(s, pl, x, w_router, bias, ids, w, logits, ws, nullptr, nullptr, st);
+  if (e == hipSuccess) e = launch_permute(s, pl, ids, pp, tiles, ws, st);
+  return e;
 }
 
 }  // namespace moe

@@ -72,7 +72,7 @@ bool make_plan(const moe_shape& s, Plan* p) {
   p->perm_off = off;
   off = align_up(off + (static_cast<size_t>(s.E) * 3 + 2 + 2 * P) * sizeof(int32_t), 256);
   p->tiles_off = off;
-  off = align_up(off + (static_cast<size_t>(p->max_tiles) * 3 + 1) * sizeof(int32_t), 256);
+  off = align_up(off + (static_cast<size_t>(p->max_tiles) * 3 + 2) * sizeof(int32_t), 256);
   p->h_off = off;
   off = align_up(off + static_cast<size_t>(P) * s.I * act_bytes(s), 256);
   p->y_off = off;
@@ -246,7 +246,7 @@ constexpr uint32_t kBadX = 1u, kBadLogits = 2u, kBadOut = 4u;
 // or, with MOE_F_FUSED_FFN, the fused kernel and the combine of its partial
 // results.
 static hipError_t ffn_and_combine(const moe_shape& s, const Plan& pl, const void* x,
-                                  const moe_experts& ex, const PermPtrs& pp, const int32_t* tiles,
+                                  const moe_experts& ex, const PermPtrs& pp, int32_t* tiles,
                                   const float* w, const void* residual, void* out, void* ws,
                                   hipStream_t st) {
   char* wsb = static_cast<char*>(ws);
@@ -258,8 +258,10 @@ static hipError_t ffn_and_combine(const moe_shape& s, const Plan& pl, const void
   }
   void* h = wsb + pl.h_off;
   void* y = wsb + pl.y_off;
-  hipError_t e = launch_ffn(s, pl, x, ex, pp.sorted_pair, tiles, h, y, st);
-  if (e == hipSuccess) e = launch_combine(s, y, pp.pair_row, w, residual, out, st);
+  hipError_t e = launch_gateup(s, pl, x, ex, pp.sorted_pair, tiles, h, st);
+  if (e == hipSuccess)
+    e = launch_down_combine(s, pl, h, ex, tiles, pp.sorted_pair, pp.pair_row, w, residual, out, y,
+                            st);
   return e;
 }
 
@@ -303,9 +305,8 @@ int layer_call(const moe_shape* shape, const void* x, const void* w_router, cons
   char* wsb = static_cast<char*>(workspace);
   if (!(s.flags & MOE_F_CHECK_FINITE)) {
     const PermPtrs pp = perm ? perm_ptrs(*perm) : ws_perm(s, pl, workspace);
-    hipError_t e = launch_route(s, pl, x, w_router, router_bias, topk_ids, topk_w, nullptr,
-                                workspace, stream);
-    if (e == hipSuccess) e = launch_permute(s, pl, topk_ids, pp, tiles, workspace, stream);
+    hipError_t e = launch_route_permute(s, pl, x, w_router, router_bias, topk_ids, topk_w, nullptr,
+                                        pp, tiles, workspace, stream);
     if (e == hipSuccess) e = ffn_and_combine(s, pl, x, *experts, pp, tiles, topk_w, residual, out, workspace, stream);
     return device_status(e);
   }
@@ -441,6 +442,37 @@ int moe_permute(const moe_shape* shape, const int32_t* topk_ids, const moe_perm*
       launch_permute(s, pl, topk_ids, perm_ptrs(*perm), ws_tiles(pl, workspace), workspace, stream));
 }
 
+int moe_route_permute(const moe_shape* shape, const void* x, const void* w_router,
+                      const float* router_bias, int32_t* topk_ids, float* topk_w, float* logits,
+                      const moe_perm* perm, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if ((st = check_ptrs({x, w_router, topk_ids, topk_w}))) return st;
+  if ((st = check_opt_ptr(router_bias)) || (st = check_opt_ptr(logits))) return st;
+  if ((st = check_perm(perm))) return st;
+  Plan pl;
+  make_plan(s, &pl);
+  if ((st = check_ws(pl, workspace, workspace_bytes))) return st;
+  const size_t P = static_cast<size_t>(s.T) * s.top_k, ab = act_bytes(s);
+  Span outs[10];
+  outs[0] = {topk_ids, P * 4};
+  outs[1] = {topk_w, P * 4};
+  outs[2] = {logits, logits ? static_cast<size_t>(s.T) * s.E * 4 : 0};
+  outs[3] = {workspace, pl.total};
+  perm_spans(s, *perm, outs + 4);
+  const Span ins[] = {{x, static_cast<size_t>(s.T) * s.H * ab},
+                      {w_router, static_cast<size_t>(s.E) * s.H * ab},
+                      {router_bias, router_bias ? s.E * 4u : 0}};
+  if (any_alias(outs, 10, ins, 3)) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  return device_status(launch_route_permute(s, pl, x, w_router, router_bias, topk_ids, topk_w,
+                                            logits, perm_ptrs(*perm), ws_tiles(pl, workspace),
+                                            workspace, stream));
+}
+
 int moe_grouped_ffn(const moe_shape* shape, const void* x, const moe_experts* experts,
                     const moe_perm* perm, void* y, void* workspace, size_t workspace_bytes,
                     hipStream_t stream) {
@@ -513,6 +545,36 @@ int moe_ffn_down(const moe_shape* shape, const void* h, const moe_experts* exper
   if (any_alias(outs, 2, ins, 7)) return MOE_E_ALIAS;
   (void)hipGetLastError();
   return device_status(launch_down(s, pl, h, *experts, ws_tiles(pl, workspace), y, stream));
+}
+
+int moe_ffn_down_combine(const moe_shape* shape, const void* h, const moe_experts* experts,
+                         const moe_perm* perm, const float* topk_w, const void* residual, void* out,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int st = check_shape(shape);
+  if (st) return st;
+  const moe_shape& s = *shape;
+  if (s.T == 0) return MOE_OK;
+  if ((st = check_ptrs({h, topk_w, out}))) return st;
+  if ((st = check_opt_ptr(residual))) return st;
+  if ((st = check_experts(s, experts))) return st;
+  if ((st = check_perm(perm))) return st;
+  Plan pl;
+  make_plan(s, &pl);
+  if ((st = check_ws(pl, workspace, workspace_bytes))) return st;
+  const size_t P = static_cast<size_t>(s.T) * s.top_k, ab = act_bytes(s);
+  Span ins[15];
+  ins[0] = {h, P * s.I * ab};
+  expert_spans(s, *experts, ins + 1);
+  perm_spans(s, *perm, ins + 7);
+  ins[13] = {topk_w, P * 4};
+  ins[14] = {residual, residual ? static_cast<size_t>(s.T) * s.H * ab : 0};
+  const Span outs[] = {{out, static_cast<size_t>(s.T) * s.H * ab}, {workspace, pl.total}};
+  if (any_alias(outs, 2, ins, 15)) return MOE_E_ALIAS;
+  (void)hipGetLastError();
+  char* wsb = static_cast<char*>(workspace);
+  return device_status(launch_down_combine(s, pl, h, *experts, ws_tiles(pl, workspace),
+                                           perm->sorted_pair, perm->pair_row, topk_w, residual,
+                                           out, wsb + pl.y_off, stream));
 }
 
 int moe_ffn_fused(const moe_shape* shape, const void* x, const moe_experts* experts,

@@ -268,3 +268,32 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 }
 
 }  // namespace moe
+
+namespace moe {
+
+// Memory operations coherent across the whole device, for data that one
+// workgroup hands to another inside a launch.  On gfx950 every XCD has its
+// own L2, and a device-scope fence (__threadfence) writes back and
+// invalidates that whole L2: thousands of workgroups doing it cost hundreds
+// of microseconds (measured: the decode down kernel with a fence per
+// workgroup took ~550 us longer).  Instead the handed-over data is stored
+// and loaded as device-scope relaxed atomics (the sc1 cache policy), and the
+// writer waits for its stores to complete before it signals with an
+// atomic.
+
+__device__ __forceinline__ void store_dev_i32(int32_t* p, int32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int32_t load_dev_i32(const int32_t* p) {
+  return __hip_atomic_load(const_cast<int32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Every memory operation this thread issued has completed (the compiler
+// keeps memory operations on their side of the wait).
+__device__ __forceinline__ void wait_memory_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+}  // namespace moe

@@ -33,7 +33,8 @@ struct Plan {
   // grouped FFN
   int nb;                 // 16-row token groups per tile (rows per tile = 16*nb)
   int max_tiles;          // upper bound on tiles: P/(16 nb) + min(E, P)
-  size_t tiles_off;       // int32 [3*max_tiles] (expert, row0, rows) + n_tiles
+  size_t tiles_off;       // int32 [3*max_tiles] (expert, row0, rows) + n_tiles + the
+                          // route + permute arrival counter
   size_t h_off;           // act [P][I] SwiGLU intermediate
   size_t y_off;           // act [P][H] expert outputs (moe_layer only)
   // MOE_F_CHECK_FINITE: private results until the status word is clean
@@ -71,7 +72,16 @@ bool router_gsum(const moe_shape& s);   // router group sums finished by the top
 hipError_t launch_route(const moe_shape& s, const Plan& pl, const void* x, const void* w_router,
                         const float* bias, int32_t* ids, float* w, float* logits, void* ws,
                         hipStream_t st);
+// route + permute in one call: fused (the top-k kernel's last workgroup
+// builds the permutation) for bf16 batches of up to 32 tokens, else the two
+// launches back to back
+bool route_permute_fused(const moe_shape& s);
+hipError_t launch_route_permute(const moe_shape& s, const Plan& pl, const void* x,
+                                const void* w_router, const float* bias, int32_t* ids, float* w,
+                                float* logits, const PermPtrs& pp, int32_t* tiles, void* ws,
+                                hipStream_t st);
 bool permute_single_pass(const moe_shape& s);
+bool permute_w1_ok(const moe_shape& s);   // the 32-token permutation (one bitmap word per expert)
 int permute_chunks(const moe_shape& s);
 hipError_t launch_permute(const moe_shape& s, const Plan& pl, const int32_t* ids,
                           const PermPtrs& pp, int32_t* tiles /* may be null */, void* ws,
@@ -88,6 +98,13 @@ bool tiles128_ok(const moe_shape& s);
 hipError_t launch_ffn(const moe_shape& s, const Plan& pl, const void* x, const moe_experts& ex,
                       const int32_t* sorted_pair, const int32_t* tiles, void* h, void* y,
                       hipStream_t st);
+// down then combine (y in `y`): with 16-row tiles of tiled bf16-activation
+// weights y goes to pair slots and the combine reads them directly
+bool down_pair_order(const moe_shape& s, const Plan& pl);
+hipError_t launch_down_combine(const moe_shape& s, const Plan& pl, const void* h,
+                               const moe_experts& ex, const int32_t* tiles,
+                               const int32_t* sorted_pair, const int32_t* pair_row, const float* w,
+                               const void* residual, void* out, void* y, hipStream_t st);
 int fused_slices(const moe_shape& s);   // I / 64
 hipError_t launch_ffn_fused(const moe_shape& s, const Plan& pl, const void* x,
                             const moe_experts& ex, const int32_t* sorted_pair,
@@ -117,6 +134,7 @@ hipError_t launch_zero_status(uint32_t* status, hipStream_t st);
 // sets `bit` in *status if any of the n values (bf16 or float32) is NaN/inf
 hipError_t launch_check_finite(const void* src, size_t n, bool bf16, uint32_t bit,
                                uint32_t* status, hipStream_t st);
+// pair_row == nullptr: y rows in pair order (row t*k + j)
 hipError_t launch_combine(const moe_shape& s, const void* y, const int32_t* pair_row,
                           const float* w, const void* residual, void* out, hipStream_t st);
 

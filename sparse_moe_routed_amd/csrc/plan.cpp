@@ -18,6 +18,8 @@ bool permute_single_pass(const moe_shape& s) {
 
 int permute_chunks(const moe_shape& s) { return (s.T + kChunkTok - 1) / kChunkTok; }
 
+bool permute_w1_ok(const moe_shape& s) { return s.T <= 32 && s.E <= 1024; }
+
 int router_parts(int H) {
   const int chunks = H / 32;
   int best = 1;

@@ -81,8 +81,9 @@ __device__ __forceinline__ void router_group_store(const double (*red)[64][4], i
 // readlanes (no LDS round trips).  -0.0 and +0.0 compare equal.  Weights:
 // exp(l_j - l_0) / sum over the selected, in float32 (the full softmax
 // renormalized over the selection).  `sel` is this wave's LDS scratch of k
-// floats.
-template <int NV>
+// floats.  DEV: the ids are stored device-coherent (another workgroup of the
+// same launch reads them).
+template <int NV, bool DEV = false>
 __device__ __forceinline__ void topk_select(const float (&v)[NV], int E, int k, float* sel,
                                             int32_t* __restrict__ ids, float* __restrict__ w) {
   const int lane = threadIdx.x & 63;
@@ -103,7 +104,10 @@ __device__ __forceinline__ void topk_select(const float (&v)[NV], int E, int k, 
     const uint32_t e = wave_min_u32(li);
     if (static_cast<int>(e & 63u) == lane) live &= ~(1u << (e >> 6));
     if (lane == 0) {
-      ids[rnk] = static_cast<int32_t>(e);
+      if constexpr (DEV)
+        store_dev_i32(ids + rnk, static_cast<int32_t>(e));
+      else
+        ids[rnk] = static_cast<int32_t>(e);
       sel[rnk] = m;
     }
   }

@@ -42,6 +42,19 @@ class MoELayerBuffers:
                               self.logits if logits else None, self.workspace, self.ws_bytes,
                               stream)
 
+    def route_permute(self, x, w_router, bias=None, logits=True, stream=None):
+        """moe_route_permute: routes into topk_ids / topk_w (and logits), the
+        permutation into this buffer's perm, the tile plan into the workspace."""
+        return _abi.moe_route_permute(self.shape, x, w_router, bias, self.topk_ids, self.topk_w,
+                                      self.logits if logits else None, self.perm, self.workspace,
+                                      self.ws_bytes, stream)
+
+    def ffn_down_combine(self, experts, residual=None, out=None, h=None, stream=None):
+        """moe_ffn_down_combine from this buffer's h into out (default self.out)."""
+        return _abi.moe_ffn_down_combine(self.shape, self.h if h is None else h, experts, self.perm,
+                                         self.topk_w, residual, self.out if out is None else out,
+                                         self.workspace, self.ws_bytes, stream)
+
     def permute(self, topk_ids=None, stream=None):
         return _abi.moe_permute(self.shape, self.topk_ids if topk_ids is None else topk_ids,
                                 self.perm, self.workspace, self.ws_bytes, stream)

@@ -50,5 +50,13 @@ hipError_t launch_check_finite(const void*, size_t, bool, uint32_t, uint32_t*, h
 }
 hipError_t launch_combine(const moe_shape&, const void*, const int32_t*, const float*, const void*,
                           void*, hipStream_t) { reached("launch_combine"); }
+hipError_t launch_route_permute(const moe_shape&, const Plan&, const void*, const void*, const float*,
+                                int32_t*, float*, float*, const PermPtrs&, int32_t*, void*,
+                                hipStream_t) { reached("launch_route_permute"); }
+hipError_t launch_down_combine(const moe_shape&, const Plan&, const void*, const moe_experts&,
+                               const int32_t*, const int32_t*, const int32_t*, const float*,
+                               const void*, void*, void*, hipStream_t) {
+  reached("launch_down_combine");
+}
 
 }  // namespace moe

@@ -30,12 +30,14 @@ def test_gateup_bytes_and_flops_closed_form():
     cfg = get_config("decode")
     U, P = 75, cfg.T * cfg.k
     b, f = bench.gateup_traffic(cfg, U)
-    assert b == U * 2 * 640 * 2560 * 2 + 8 * 2560 * 2 + P * 640 * 2
+    # the weights of the active experts and the token rows; the intermediate
+    # the kernel writes is scratch and not counted
+    assert b == U * 2 * 640 * 2560 * 2 + 8 * 2560 * 2
     assert f == 2.0 * P * 2 * 640 * 2560
     # gate + up are two thirds of an expert record
     cfg4 = get_config("stack_int4")
     b4, _ = bench.gateup_traffic(cfg4, 1)
-    assert b4 - cfg4.T * cfg4.H * 2 - cfg4.T * cfg4.k * cfg4.I * 2 == pytest.approx(2_764_800 * 2 / 3)
+    assert b4 - cfg4.T * cfg4.H * 2 == pytest.approx(2_764_800 * 2 / 3)
 
 
 def test_digest_ignores_comments_not_code():
@@ -62,6 +64,20 @@ def test_traffic_only_for_the_recorded_digest(workload):
     t = bench.traffic_from_profiles(workload, recorded)
     assert t is not None and t > 0
     assert bench.traffic_from_profiles(workload, "0" * 16) is None
+
+
+def test_default_run_covers_every_workload():
+    assert set(bench.OTHER_WORKLOADS) | {"decode"} == {"tiny", "decode", "prefill", "stack_int4",
+                                                      "verify_int2"}
+    line = {"value": 1.0, "unit": "tokens/s", "steps": 2, "warmup": 1, "ms_per_step": 1.0,
+            "dtype": "bf16", "config": {}, "timing": {}, "layer_hbm": {}, "graph": None,
+            "cpu_baseline": None, "oracle_route_check": None, "route_locality": {},
+            "roofline": {k: 0 for k in ("bound", "achieved", "peak", "unit", "frac", "traffic",
+                                        "kernel", "avg_launch_us", "hbm_frac", "mfma_frac",
+                                        "attainable_frac", "kernel_source_digest")}}
+    s = bench.summarize(line)
+    assert "route_locality" not in s and "kernel_source_digest" not in s["roofline"]
+    assert s["roofline"]["attainable_frac"] == 0 and s["oracle_route_check"] is None
 
 
 def test_more_than_one_gpu_is_refused():

@@ -498,30 +498,6 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
       for (int j = 0; j < 4; ++j) orow[b][j] = out_row(min(b * 16 + 4 * q4 + j, tl.rows - 1));
   }
   const int hp = 2 * I + 16;   // SH: LDS row pitch in bytes (rows 16 bytes = 4 banks apart)
-  if constexpr (SH) {
-    // 16-byte chunks; rows past the tile repeat its last row (never stored)
-    const int cpr = I / 8, nch = 16 * NB * cpr;
-    for (int c0 = threadIdx.x; c0 < nch; c0 += 4 * 256) {
-      u32x4_t v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = c0 + i * 256;
-        if (c < nch) {
-          const int row = c / cpr, c8 = c - row * cpr;
-          v[i] = ld16(h + static_cast<size_t>(tl.row0 + min(row, tl.rows - 1)) * I + c8 * 8);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c = c0 + i * 256;
-        if (c < nch) {
-          const int row = c / cpr, c8 = c - row * cpr;
-          *reinterpret_cast<u32x4_t*>(hs + row * hp + c8 * 16) = v[i];
-        }
-      }
-    }
-    __syncthreads();
-  }
   // wave index as a uniform value (the slab base below must live in SGPRs)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
@@ -598,7 +574,42 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
       }
     }
   };
-  unit_loop<PF, Stage>(0, I / 128, load, compute);
+  auto stage_h = [&]() {
+    // 16-byte chunks; rows past the tile repeat its last row (never stored)
+    const int cpr = I / 8, nch = 16 * NB * cpr;
+    for (int c0 = threadIdx.x; c0 < nch; c0 += 4 * 256) {
+      u32x4_t v[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = c0 + i * 256;
+        if (c < nch) {
+          const int row = c / cpr, c8 = c - row * cpr;
+          v[i] = ld16(h + static_cast<size_t>(tl.row0 + min(row, tl.rows - 1)) * I + c8 * 8);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int c = c0 + i * 256;
+        if (c < nch) {
+          const int row = c / cpr, c8 = c - row * cpr;
+          *reinterpret_cast<u32x4_t*>(hs + row * hp + c8 * 16) = v[i];
+        }
+      }
+    }
+    __syncthreads();
+  };
+  if constexpr (SH && !PF) {
+    // the first unit's weights are in flight while the rows are staged
+    Stage s0;
+    load(s0, 0);
+    stage_h();
+    SCHED_FENCE();
+    compute(s0);
+    unit_loop<false, Stage>(1, I / 128, load, compute);
+  } else {
+    if constexpr (SH) stage_h();
+    unit_loop<PF, Stage>(0, I / 128, load, compute);
+  }
   if constexpr (kStageOut) {
     store_tile_rows<NB, MB>(ot, [&](int mb, int b, int j) { return acc[mb][b][j]; }, tl.rows,
                             [&](int row, int col, u32x4_t v) {

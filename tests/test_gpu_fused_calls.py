@@ -34,6 +34,8 @@ CASES = {
     "int4_T5": C4.with_(T=5, H=512, E=64, I=128, k=8, layers=1),
     "ragged_E": C2.with_(T=19, H=384, E=100, I=128, k=7),
     "E1024_k32": C2.with_(T=24, H=256, E=1024, I=128, k=32),
+    "hot_bf16_T32": C5.with_(T=32, H=1024, E=96, I=256, wfmt="dense", layers=1),  # 2-tile experts
+    "pairs_510": C2.with_(T=51, H=512, E=256, I=128),                     # 16-row tiles, many experts
     "prefill_small": C3.with_(T=200, H=256, I=128),                      # two launches
     "tiny_f32": C1,                                                       # float32: two launches
 }

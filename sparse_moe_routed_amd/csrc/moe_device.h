@@ -254,6 +254,17 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return min(min(r0, r1), min(r2, r3));
 }
 
+// Maximum of an unsigned value over the wave (wave-uniform result).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppXor1>(v));
+  v = max(v, dpp_u32<kDppXor2>(v));
+  v = max(v, dpp_u32<kDppHalfMirror>(v));
+  v = max(v, dpp_u32<kDppMirror>(v));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
 // Sum of a float over the wave in a fixed association (wave-uniform result).
 __device__ __forceinline__ float wave_sum_f32(float v) {
   v += __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(v)));

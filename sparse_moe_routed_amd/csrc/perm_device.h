@@ -21,10 +21,12 @@ namespace moe {
 // workspace needs no initialisation.
 
 // LDS of permute_w1_body.
+constexpr int kPermW1KeepPairs = 2048;   // routes kept in LDS between the two passes
 struct PermW1Lds {
-  uint32_t bits[1024];   // token bitmap per expert (T <= 32)
-  int off[1024];         // first row of each expert
-  int wtot[4][3];        // per-wave totals of (rows, active experts, tiles)
+  uint32_t bits[1024];                // token bitmap per expert (T <= 32)
+  int off[1024];                      // first row of each expert
+  int wtot[4][3];                     // per-wave totals of (rows, active experts, tiles)
+  int32_t ids[kPermW1KeepPairs];      // the routes, when P <= kPermW1KeepPairs
 };
 
 // Up to 32 tokens (one bitmap word per expert; decode and verifier blocks),
@@ -54,8 +56,10 @@ __device__ __forceinline__ void permute_w1_body(const int32_t* ids, int T, int k
   for (int i = 0; i < 4; ++i)
     if (i < ept && e0 + i < E) L.bits[e0 + i] = 0u;
   __syncthreads();
+  const bool keep = P <= kPermW1KeepPairs;   // the second pass reads the routes from LDS
   for (int p = tid; p < P; p += 256) {
     const int e = DEV ? load_dev_i32(ids + p) : ids[p];
+    if (keep) L.ids[p] = e;
     if (e >= 0 && e < E) atomicOr(&L.bits[e], 1u << (p / k));
   }
   __syncthreads();
@@ -127,7 +131,7 @@ __device__ __forceinline__ void permute_w1_body(const int32_t* ids, int T, int k
   }
   __syncthreads();
   for (int p = tid; p < P; p += 256) {
-    const int e = DEV ? load_dev_i32(ids + p) : ids[p];
+    const int e = keep ? L.ids[p] : (DEV ? load_dev_i32(ids + p) : ids[p]);
     if (e < 0 || e >= E) continue;
     const int t = p / k;
     const int row = L.off[e] + __popc(L.bits[e] & ((1u << t) - 1u));

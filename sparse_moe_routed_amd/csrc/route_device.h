@@ -73,19 +73,35 @@ __device__ __forceinline__ void router_group_store(const double (*red)[64][4], i
   }
 }
 
-// Exact top-k of one token by one wave; lane l holds the logits v[j] of
-// experts j*64 + l (NV slots, E <= 64 NV; slots at or past E are ignored).
-// Each of the k rounds takes the wave maximum m of the remaining logits,
+// Order-preserving integer key of a logit: a > b (as floats) exactly when
+// key(a) > key(b); -0.0 keys as +0.0 (the two compare equal), NaN keys as 0,
+// below every other value, and every other value keys above 0.
+__device__ __forceinline__ uint32_t logit_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  const uint32_t kk = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return f != f ? 0u : kk;
+}
+__device__ __forceinline__ float logit_of_key(uint32_t kk) {
+  return __uint_as_float((kk & 0x80000000u) ? (kk & 0x7fffffffu) : ~kk);
+}
+
+// LDS written by lanes of this wave is visible to its other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The selection of topk_select by k rounds (any k; the fallback of
+// topk_threshold): each of the k rounds takes the wave maximum m of the remaining logits,
 // then the smallest expert index whose logit equals m -- the total order
 // (logit descending, index ascending) -- with DPP row reductions and
-// readlanes (no LDS round trips).  -0.0 and +0.0 compare equal.  Weights:
-// exp(l_j - l_0) / sum over the selected, in float32 (the full softmax
-// renormalized over the selection).  `sel` is this wave's LDS scratch of k
-// floats.  DEV: the ids are stored device-coherent (another workgroup of the
-// same launch reads them).
-template <int NV, bool DEV = false>
-__device__ __forceinline__ void topk_select(const float (&v)[NV], int E, int k, float* sel,
-                                            int32_t* __restrict__ ids, float* __restrict__ w) {
+// readlanes (no LDS round trips).  -0.0 and +0.0 compare equal.  Writes ids[r] and
+// sel[r] (the logit) for every rank r < k.
+template <int NV, bool DEV>
+__device__ __forceinline__ void topk_rounds(const float (&v)[NV], int E, int k, float* sel,
+                                            int32_t* __restrict__ ids) {
   const int lane = threadIdx.x & 63;
   uint32_t live = 0;
 #pragma unroll
@@ -110,6 +126,109 @@ __device__ __forceinline__ void topk_select(const float (&v)[NV], int E, int k, 
         ids[rnk] = static_cast<int32_t>(e);
       sel[rnk] = m;
     }
+  }
+}
+
+// The selection of topk_select for k <= 64 without k dependent rounds.  With
+// integer keys (logit_key; ignored slots key as 0) and lane maxima m_l:
+// tau = the k-th largest m_l (each lane counts the maxima >= its own from
+// LDS; tau is the largest m_l whose count reaches k).  The k lanes holding
+// the k largest maxima give k distinct logits >= tau, so the k-th largest
+// logit is >= tau and every logit of the top k has key >= tau.  The keys >=
+// tau (the candidates, each with its expert index) are packed into LDS in
+// lane order, and every candidate's rank is the number of candidates
+// before it in the total order (key descending, index ascending) -- the
+// rank it has among all logits, since everything before it is a
+// candidate too.  Ranks below k give ids[r] and sel[r].  Returns false,
+// having written no id, when fewer than k logits are selectable (tau = 0)
+// or more than 64 keys reach tau (massive ties); sel[0 .. 191] is scratch.
+template <int NV, bool DEV>
+__device__ __forceinline__ bool topk_threshold(const float (&v)[NV], int E, int k, float* sel,
+                                               int32_t* __restrict__ ids) {
+  const int lane = threadIdx.x & 63;
+  uint32_t key[NV];
+  uint32_t lm = 0u;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    key[j] = (j * 64 + lane < E) ? logit_key(v[j]) : 0u;
+    lm = max(lm, key[j]);
+  }
+  uint32_t* S = reinterpret_cast<uint32_t*>(sel);
+  S[lane] = lm;
+  wave_lds_sync();
+  uint32_t cc[4] = {0u, 0u, 0u, 0u};   // four independent count chains
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const u32x4_t a = reinterpret_cast<const u32x4_t*>(S)[q];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) cc[i] += a[i] >= lm ? 1u : 0u;
+  }
+  const uint32_t c = (cc[0] + cc[1]) + (cc[2] + cc[3]);
+  const uint32_t tau = wave_max_u32(c >= static_cast<uint32_t>(k) ? lm : 0u);
+  if (tau == 0u) return false;
+  uint32_t bits = 0u;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) bits |= (key[j] >= tau ? 1u : 0u) << j;
+  const uint32_t cnt = __popc(bits);
+  // exclusive prefix of the per-lane counts (<= 16: five bit planes)
+  uint32_t pre = 0u, C = 0u;
+#pragma unroll
+  for (int b = 0; b < 5; ++b) {
+    const uint64_t m = __ballot((cnt >> b) & 1u);
+    pre += __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u))
+           << b;
+    C += static_cast<uint32_t>(__popcll(m)) << b;
+  }
+  if (C > 64u) return false;
+  uint32_t* ck = S + 64;    // candidate keys
+  uint32_t* ci = S + 128;   // candidate expert indices
+  uint32_t pos = pre;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    if ((bits >> j) & 1u) {
+      ck[pos] = key[j];
+      ci[pos] = static_cast<uint32_t>(j * 64 + lane);
+      ++pos;
+    }
+  }
+  wave_lds_sync();
+  if (static_cast<uint32_t>(lane) < C) {
+    const uint32_t kl = ck[lane], il = ci[lane];
+    uint32_t rank = 0u;
+    for (uint32_t q = 0; q < (C + 3u) / 4u; ++q) {
+      const u32x4_t a = reinterpret_cast<const u32x4_t*>(ck)[q];
+      const u32x4_t b = reinterpret_cast<const u32x4_t*>(ci)[q];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        rank += (4u * q + i < C && (a[i] > kl || (a[i] == kl && b[i] < il))) ? 1u : 0u;
+    }
+    if (rank < static_cast<uint32_t>(k)) {
+      if constexpr (DEV)
+        store_dev_i32(ids + rank, static_cast<int32_t>(il));
+      else
+        ids[rank] = static_cast<int32_t>(il);
+      sel[rank] = logit_of_key(kl);   // over the lane maxima, no longer read
+    }
+  }
+  return true;
+}
+
+// Exact top-k of one token by one wave; lane l holds the logits v[j] of
+// experts j*64 + l (NV slots, E <= 64 NV; slots at or past E are ignored),
+// in the total order (logit descending, index ascending; -0.0 and +0.0
+// compare equal): topk_threshold for k <= 64, else (or when it cannot
+// decide) topk_rounds.  Weights: exp(l_j - l_0) / sum over the selected, in
+// float32 (the full softmax renormalized over the selection).  `sel` is this
+// wave's LDS scratch of max(k, 192) floats.  DEV: the ids are stored
+// device-coherent (another workgroup of the same launch reads them).
+template <int NV, bool DEV = false>
+__device__ __forceinline__ void topk_select(const float (&v)[NV], int E, int k, float* sel,
+                                            int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int lane = threadIdx.x & 63;
+  if (!(k <= 64 && topk_threshold<NV, DEV>(v, E, k, sel, ids))) {
+    wave_lds_sync();
+    topk_rounds<NV, DEV>(v, E, k, sel, ids);
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -10,7 +10,7 @@ the C ABI, bit for bit:
 on both sides of the size limits of the single-launch paths (up to 32
 tokens, bf16, tiled weights with 16-row tiles), with and without a residual,
 for every weight format, and on repeated calls that reuse one workspace (the
-arrival counters must come back to zero by themselves).  Parity of the layer
+tile plan must be rewritten in full each time).  Parity of the layer
 against the oracle on these paths is covered by the moe_layer tests, which
 run them."""
 import numpy as np
@@ -34,6 +34,7 @@ CASES = {
     "int4_T5": C4.with_(T=5, H=512, E=64, I=128, k=8, layers=1),
     "ragged_E": C2.with_(T=19, H=384, E=100, I=128, k=7),
     "E1024_k32": C2.with_(T=24, H=256, E=1024, I=128, k=32),
+    "k80": C2.with_(T=4, H=256, E=96, I=128, k=80),                      # top-k past 64: three launches
     "hot_bf16_T32": C5.with_(T=32, H=1024, E=96, I=256, wfmt="dense", layers=1),  # 2-tile experts
     "pairs_510": C2.with_(T=51, H=512, E=256, I=128),                     # 16-row tiles, many experts
     "prefill_small": C3.with_(T=200, H=256, I=128),                      # two launches
@@ -59,7 +60,7 @@ def test_route_permute_equals_route_then_permute(name):
     say(f"[{name}] moe_route + moe_permute vs moe_route_permute (tiled={tiled})")
     a.route(case.li.x, case.li.w_router, case.li.bias)
     a.permute()
-    for rep in range(2):     # the second call reuses the workspace and its counters
+    for rep in range(2):     # the second call reuses the workspace
         for t in (b.topk_ids, b.counts, b.offsets, b.sorted_pair, b.pair_row, b.active, b.n_active):
             t.fill_(-7)
         b.route_permute(case.li.x, case.li.w_router, case.li.bias)
@@ -91,7 +92,7 @@ def test_down_combine_equals_down_then_combine(name):
         buf.ffn_down(ex)
         ref = torch.empty_like(buf.out)
         buf.combine(residual=residual, out=ref)
-        for rep in range(3):     # counters reset by the last workgroup of each slice
+        for rep in range(3):     # repeated calls on one workspace
             out = torch.full_like(buf.out, float("nan"))
             buf.ffn_down_combine(ex, residual=residual, out=out)
             torch.cuda.synchronize()

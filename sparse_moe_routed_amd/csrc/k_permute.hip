@@ -19,25 +19,15 @@
 
 namespace moe {
 
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int n = __shfl_up(v, off, kWave);
-    if (lane >= off) v += n;
-  }
-  return v;
-}
-
 // Exclusive scan over a 1024-thread block; every thread must call it.
 __device__ int block_excl_scan(int v, int* s_tot, int* total) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int inc = wave_incl_scan(v);
+  const int inc = wave_incl_scan_i32(v);
   if (lane == 63) s_tot[wave] = inc;
   __syncthreads();
   if (wave == 0) {
     const int tv = lane < 16 ? s_tot[lane] : 0;
-    const int ti = wave_incl_scan(tv);
+    const int ti = wave_incl_scan_i32(tv);
     if (lane < 16) s_tot[lane] = ti - tv;
     if (lane == 15) s_tot[16] = ti;
   }

@@ -265,6 +265,20 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return max(max(r0, r1), max(r2, r3));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in VALU: DPP row
+// shifts by 1, 2, 4, 8 scan each row of 16 lanes, then lane 15 of rows 0
+// and 2 is added to rows 1 and 3 and lane 31 to rows 2 and 3 (row
+// broadcasts).  Lanes without a source in a step add nothing.
+__device__ __forceinline__ int wave_incl_scan_i32(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
 // Sum of a float over the wave in a fixed association (wave-uniform result).
 __device__ __forceinline__ float wave_sum_f32(float v) {
   v += __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(v)));

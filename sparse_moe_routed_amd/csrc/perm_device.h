@@ -73,17 +73,7 @@ __device__ __forceinline__ void permute_w1_body(const int32_t* ids, int T, int k
     N += n[i];
   }
   // inclusive wave scans of the three per-thread sums, then wave offsets
-  int iC = C, iF = F, iN = N;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int a = __shfl_up(iC, off, kWave), b = __shfl_up(iF, off, kWave),
-              d = __shfl_up(iN, off, kWave);
-    if (lane >= off) {
-      iC += a;
-      iF += b;
-      iN += d;
-    }
-  }
+  const int iC = wave_incl_scan_i32(C), iF = wave_incl_scan_i32(F), iN = wave_incl_scan_i32(N);
   if (lane == 63) {
     L.wtot[wave][0] = iC;
     L.wtot[wave][1] = iF;

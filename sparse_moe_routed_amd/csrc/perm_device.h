@@ -63,11 +63,14 @@ __device__ __forceinline__ void permute_w1_body(const int32_t* ids, int T, int k
     if (e >= 0 && e < E) atomicOr(&L.bits[e], 1u << (p / k));
   }
   __syncthreads();
+  // rows per tile are 16 nb (a power of two): a shift instead of a division
+  const bool pow2 = (rt & (rt - 1)) == 0;
+  const int rsh = __ffs(rt) - 1;
   int c[4], n[4], C = 0, F = 0, N = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     c[i] = (i < ept && e0 + i < E) ? __popc(L.bits[e0 + i]) : 0;
-    n[i] = (c[i] + rt - 1) / rt;
+    n[i] = pow2 ? (c[i] + rt - 1) >> rsh : (c[i] + rt - 1) / rt;
     C += c[i];
     F += c[i] > 0 ? 1 : 0;
     N += n[i];

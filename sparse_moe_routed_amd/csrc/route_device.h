@@ -98,11 +98,11 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // The selection of topk_select by k rounds (any k; the fallback of
-// topk_threshold): each of the k rounds takes the wave maximum m of the remaining logits,
-// then the smallest expert index whose logit equals m -- the total order
-// (logit descending, index ascending) -- with DPP row reductions and
-// readlanes (no LDS round trips).  -0.0 and +0.0 compare equal.  Writes ids[r] and
-// sel[r] (the logit) for every rank r < k.
+// topk_threshold): each round takes the wave maximum m of the remaining
+// logits, then the smallest expert index whose logit equals m -- the total
+// order (logit descending, index ascending) -- with DPP row reductions and
+// readlanes (no LDS round trips).  -0.0 and +0.0 compare equal.  Writes
+// ids[r] and sel[r] (the logit) for every rank r < k.
 template <int NV, bool DEV>
 __device__ __forceinline__ void topk_rounds(const float (&v)[NV], int E, int k, float* sel,
                                             int32_t* __restrict__ ids) {

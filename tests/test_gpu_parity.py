@@ -41,6 +41,10 @@ SMALL = {
     # LDS-staged router with a ragged expert tile and parts that end inside
     # a 128-wide k unit (H/32 = 20 chunks, 10 parts of 2)
     "router_ragged_parts": C3.with_(T=200, H=640, E=100, I=128, k=6),
+    # top-k at the edges of the threshold selection: k = 64 of 64 experts
+    # (64 candidates, the most it ranks directly), k = 65 (k rounds)
+    "topk_k64": C2.with_(T=20, H=256, E=64, I=128, k=64),
+    "topk_k65": C2.with_(T=20, H=256, E=80, I=128, k=65),
 }
 
 _cache = {}

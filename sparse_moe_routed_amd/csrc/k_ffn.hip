@@ -22,6 +22,8 @@
 // Low-bit weights: one MFMA per group of 32 codes (codes -> exact bf16
 // integers), the float32 group partial is multiplied by the fp16 scale and
 // accumulated in float32.
+#include <type_traits>
+
 #include "ffn_tiled.h"
 #include "moe_device.h"
 #include "moe_internal.h"
@@ -317,6 +319,13 @@ __global__ __launch_bounds__(256) void k_down(const uint16_t* __restrict__ h,
 // so each group partial is sum(q x) before its fp16 scale is applied.
 // 1-D grid over (tile, slice) items, I / (16 MB 4 / KSPLIT) slices per tile;
 // block 256.
+// Low-bit gate/up with one token block per tile: weight loads rolled a unit
+// ahead in place (see k_gateup_t).
+template <int WF, int NB>
+constexpr bool kRollLowBit() {
+  return WF != WF_BF16 && NB == 1;
+}
+
 template <int WF, int NB, int KSPLIT, int MB, bool PF>
 __global__ __launch_bounds__(256) void k_gateup_t(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
@@ -411,7 +420,72 @@ __global__ __launch_bounds__(256) void k_gateup_t(
       }
     }
   };
-  unit_loop<PF, Stage>(ub, ub + units, load, compute);
+  if constexpr (kRollLowBit<WF, NB>()) {
+    // low-bit, one token block: the loads of a (row block, gate/up) pair
+    // for unit u+1 are issued into its registers as soon as unit u is done
+    // with them, and the token fragments of unit u+1 at the start of unit
+    // u, so every load has one unit of multiplies to arrive in, without a
+    // second register stage.  Per accumulator the additions run in the same
+    // order as in compute() (chunk order within a unit, units in order).
+    TScales sc[MB][2];
+    TRaw<WF> raw[MB][2];
+    u32x4_t xa[4], xn[4];
+    auto load_pair = [&](int mb, int gu, int u) {
+      const Slab<WF>& S = gu == 0 ? Sg : Su;
+      sc[mb][gu] = tscales<WF, weight_aux<NB>()>(S, mb, u, r);
+      raw[mb][gu] = tload<WF, weight_aux<NB>()>(S, mb, u, lane);
+    };
+    auto load_x = [&](u32x4_t (&xv)[4], int u) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) xv[st] = ld16(px[0] + 128 * u + 32 * st);
+    };
+    // ROLL: the loads of unit u + 1 go out as unit u's registers free up
+    auto unit = [&](int u, auto roll_tag) {
+      constexpr bool ROLL = decltype(roll_tag)::value;
+      if constexpr (ROLL) load_x(xn, u + 1);
+      f32x4_t corr[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        corr[st] = mfma_bf16(xa[st], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int gu = 0; gu < 2; ++gu) {
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const u32x4_t wv = tdecode<WF>(raw[mb][gu], st, dq);
+            const float sv = sc[mb][gu].f32(st);
+            const f32x4_t pp = mfma_bf16(xa[st], wv, corr[st]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[mb][gu][0][j] = fmaf(sv, pp[j], acc[mb][gu][0][j]);
+          }
+          if constexpr (ROLL) {
+            SCHED_FENCE();
+            load_pair(mb, gu, u + 1);
+            SCHED_FENCE();
+          }
+        }
+      }
+      if constexpr (ROLL) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) xa[st] = xn[st];
+      }
+    };
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      load_pair(mb, 0, ub);
+      load_pair(mb, 1, ub);
+    }
+    load_x(xa, ub);
+    SCHED_FENCE();
+    // the last unit is peeled off so that every load in the loop body is
+    // unconditional (a load under a branch makes the compiler wait for all
+    // outstanding loads where it needs any of them)
+    for (int u = ub; u + 1 < ub + units; ++u) unit(u, std::true_type{});
+    unit(ub + units - 1, std::false_type{});
+  } else {
+    unit_loop<PF, Stage>(ub, ub + units, load, compute);
+  }
 
   if constexpr (KSPLIT > 1) {
 #pragma unroll
@@ -598,7 +672,53 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
     }
     __syncthreads();
   };
-  if constexpr (SH && !PF) {
+  if constexpr (SH && kRollLowBit<WF, NB>()) {
+    // low-bit, one token block, rows in LDS: the loads of row block mb for
+    // unit u+1 are issued into its registers as soon as unit u is done with
+    // them (as in k_gateup_t), so every weight load has one unit of
+    // multiplies to arrive in.  Per accumulator the additions run in the
+    // order of compute() (chunk order within a unit, units in order).
+    TScales sc[MB];
+    TRaw<WF> raw[MB];
+    auto load_blk = [&](int mb, int u) {
+      sc[mb] = tscales<WF, weight_aux<NB>()>(Sd, mb, u, r);
+      raw[mb] = tload<WF, weight_aux<NB>()>(Sd, mb, u, lane);
+    };
+    auto unit = [&](int u, auto roll_tag) {
+      constexpr bool ROLL = decltype(roll_tag)::value;
+      u32x4_t ha[4];
+      f32x4_t corr[4];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        ha[st] = *reinterpret_cast<const u32x4_t*>(hs + r * hp + (128 * u + 32 * st + 8 * q) * 2);
+        corr[st] = mfma_bf16(ha[st], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const u32x4_t wv = tdecode<WF>(raw[mb], st, dq);
+          const float sv = sc[mb].f32(st);
+          const f32x4_t pp = mfma_bf16(ha[st], wv, corr[st]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[mb][0][j] = fmaf(sv, pp[j], acc[mb][0][j]);
+        }
+        if constexpr (ROLL) {
+          SCHED_FENCE();
+          load_blk(mb, u + 1);
+          SCHED_FENCE();
+        }
+      }
+    };
+    // the first unit's weights are in flight while the rows are staged
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) load_blk(mb, 0);
+    stage_h();
+    SCHED_FENCE();
+    const int nu = I / 128;
+    for (int u = 0; u + 1 < nu; ++u) unit(u, std::true_type{});
+    unit(nu - 1, std::false_type{});
+  } else if constexpr (SH && !PF) {
     // the first unit's weights are in flight while the rows are staged
     Stage s0;
     load(s0, 0);

@@ -102,6 +102,16 @@ __device__ __forceinline__ bool single_tile(const int32_t* __restrict__ tiles, i
   return (ti == 0 || tiles[3 * (ti - 1)] != e) && (ti + 1 >= n || tiles[3 * (ti + 1)] != e);
 }
 
+// The 4-row layout of a 16-row token block holding at most 4 rows (low-bit
+// kernels): token t feeds the MFMA's A rows 4t .. 4t+3, so output component
+// 0 of lane quarter q is token q and each product needs one scale FMA
+// instead of four (in the 16-row layout A row r is token r and all four
+// components of a lane are distinct rows).  The tile row that accumulator
+// component j of lane quarter q belongs to, in either layout:
+__device__ __forceinline__ int acc_row(bool spread, int q, int j) {
+  return spread ? 4 * j + q : 4 * q + j;
+}
+
 // The bf16 output tile of a 256-thread item -- rows 0 .. 16 NB - 1 of the
 // tile, columns col0 .. col0 + 64 MB - 1 -- written through LDS: value(mb, b,
 // j) of lane (r, q) in wave w is row 16 b + 4 q + j, column 16 (MB w + mb) +
@@ -114,9 +124,10 @@ constexpr int out_tile_bytes() {
 }
 // With a store functor: store(row, col, v) writes the 16 bytes v of tile row
 // `row` at column `col` (8 values) wherever the caller keeps them.
+// `spread`: the accumulators are in the 4-row layout (acc_row).
 template <int NB, int MB, typename Val, typename Store>
 __device__ __forceinline__ void store_tile_rows(char* lds, Val&& val, int rows, Store store,
-                                                int col0) {
+                                                int col0, bool spread = false) {
   constexpr int pitch = 128 * MB + 16;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
@@ -127,7 +138,7 @@ __device__ __forceinline__ void store_tile_rows(char* lds, Val&& val, int rows, 
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint16_t*>(lds + (16 * b + 4 * q + j) * pitch +
+        *reinterpret_cast<uint16_t*>(lds + (16 * b + acc_row(spread, q, j)) * pitch +
                                      (16 * (MB * wave + mb) + r) * 2) = f32_to_bf16(val(mb, b, j));
   __syncthreads();
   constexpr int segs = 8 * MB;          // 16-byte segments per row

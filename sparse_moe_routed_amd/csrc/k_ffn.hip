@@ -420,6 +420,8 @@ __global__ __launch_bounds__(256) void k_gateup_t(
       }
     }
   };
+  // low-bit tiles of at most 4 rows take the 4-row layout (spread_rows)
+  const bool spread = kRollLowBit<WF, NB>() && tl.rows <= 4;
   if constexpr (kRollLowBit<WF, NB>()) {
     // low-bit, one token block: the loads of a (row block, gate/up) pair
     // for unit u+1 are issued into its registers as soon as unit u is done
@@ -427,62 +429,84 @@ __global__ __launch_bounds__(256) void k_gateup_t(
     // u, so every load has one unit of multiplies to arrive in, without a
     // second register stage.  Per accumulator the additions run in the same
     // order as in compute() (chunk order within a unit, units in order).
-    TScales sc[MB][2];
-    TRaw<WF> raw[MB][2];
-    u32x4_t xa[4], xn[4];
-    auto load_pair = [&](int mb, int gu, int u) {
-      const Slab<WF>& S = gu == 0 ? Sg : Su;
-      sc[mb][gu] = tscales<WF, weight_aux<NB>()>(S, mb, u, r);
-      raw[mb][gu] = tload<WF, weight_aux<NB>()>(S, mb, u, lane);
-    };
-    auto load_x = [&](u32x4_t (&xv)[4], int u) {
+    // SP: the 4-row layout, one scale FMA per product instead of four.
+    auto rolled = [&](auto sp_tag) {
+      constexpr bool SP = decltype(sp_tag)::value;
+      const uint16_t* pxr;
+      {
+        const int rr = min(SP ? (r >> 2) : r, tl.rows - 1);
+        int p = sorted_pair[tl.row0 + rr];
+        p = min(max(p, 0), P - 1);
+        pxr = x + static_cast<size_t>(p / k) * H + q * 8;
+      }
+      TScales sc[MB][2];
+      TRaw<WF> raw[MB][2];
+      u32x4_t xa[4], xn[4];
+      auto load_pair = [&](int mb, int gu, int u) {
+        const Slab<WF>& S = gu == 0 ? Sg : Su;
+        sc[mb][gu] = tscales<WF, weight_aux<NB>()>(S, mb, u, r);
+        raw[mb][gu] = tload<WF, weight_aux<NB>()>(S, mb, u, lane);
+      };
+      auto load_x = [&](u32x4_t (&xv)[4], int u) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) xv[st] = ld16(px[0] + 128 * u + 32 * st);
-    };
-    // ROLL: the loads of unit u + 1 go out as unit u's registers free up
-    auto unit = [&](int u, auto roll_tag) {
-      constexpr bool ROLL = decltype(roll_tag)::value;
-      if constexpr (ROLL) load_x(xn, u + 1);
-      f32x4_t corr[4];
+        for (int st = 0; st < 4; ++st) xv[st] = ld16(pxr + 128 * u + 32 * st);
+      };
+      // ROLL: the loads of unit u + 1 go out as unit u's registers free up
+      auto unit = [&](int u, auto roll_tag) {
+        constexpr bool ROLL = decltype(roll_tag)::value;
+        if constexpr (ROLL) load_x(xn, u + 1);
+        f32x4_t corr[4];
 #pragma unroll
-      for (int st = 0; st < 4; ++st)
-        corr[st] = mfma_bf16(xa[st], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+        for (int st = 0; st < 4; ++st)
+          corr[st] = mfma_bf16(xa[st], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
+        for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-        for (int gu = 0; gu < 2; ++gu) {
+          for (int gu = 0; gu < 2; ++gu) {
 #pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            const u32x4_t wv = tdecode<WF>(raw[mb][gu], st, dq);
-            const float sv = sc[mb][gu].f32(st);
-            const f32x4_t pp = mfma_bf16(xa[st], wv, corr[st]);
+            for (int st = 0; st < 4; ++st) {
+              const u32x4_t wv = tdecode<WF>(raw[mb][gu], st, dq);
+              const float sv = sc[mb][gu].f32(st);
+              const f32x4_t pp = mfma_bf16(xa[st], wv, corr[st]);
+              if constexpr (SP) {
+                acc[mb][gu][0][0] = fmaf(sv, pp[0], acc[mb][gu][0][0]);
+              } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[mb][gu][0][j] = fmaf(sv, pp[j], acc[mb][gu][0][j]);
-          }
-          if constexpr (ROLL) {
-            SCHED_FENCE();
-            load_pair(mb, gu, u + 1);
-            SCHED_FENCE();
+                for (int j = 0; j < 4; ++j) acc[mb][gu][0][j] = fmaf(sv, pp[j], acc[mb][gu][0][j]);
+              }
+            }
+            SCHED_FENCE();   // pair by pair: each waits for its own loads only
+            if constexpr (ROLL) {
+              load_pair(mb, gu, u + 1);
+              SCHED_FENCE();
+            }
           }
         }
-      }
-      if constexpr (ROLL) {
+        if constexpr (ROLL) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) xa[st] = xn[st];
+          for (int st = 0; st < 4; ++st) xa[st] = xn[st];
+        }
+      };
+      // the token fragments first, as in the loop body: with the loads
+      // issued in the same order on both paths into the loop, each pair
+      // waits for its own loads only (given the other order here, the
+      // compiler waits for every outstanding load at the top of each unit)
+      load_x(xa, ub);
+      SCHED_FENCE();
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        load_pair(mb, 0, ub);
+        load_pair(mb, 1, ub);
+        SCHED_FENCE();
       }
+      // the last unit is peeled off so that every load in the loop body is
+      // unconditional (a load under a branch makes the compiler wait for all
+      // outstanding loads where it needs any of them)
+      for (int u = ub; u + 1 < ub + units; ++u) unit(u, std::true_type{});
+      unit(ub + units - 1, std::false_type{});
     };
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      load_pair(mb, 0, ub);
-      load_pair(mb, 1, ub);
-    }
-    load_x(xa, ub);
-    SCHED_FENCE();
-    // the last unit is peeled off so that every load in the loop body is
-    // unconditional (a load under a branch makes the compiler wait for all
-    // outstanding loads where it needs any of them)
-    for (int u = ub; u + 1 < ub + units; ++u) unit(u, std::true_type{});
-    unit(ub + units - 1, std::false_type{});
+    if (spread) rolled(std::true_type{});
+    else rolled(std::false_type{});
   } else {
     unit_loop<PF, Stage>(ub, ub + units, load, compute);
   }
@@ -510,7 +534,7 @@ __global__ __launch_bounds__(256) void k_gateup_t(
         const int i = (sl * RG + g_) * 16 * MB + (m0 + mm) * 16 + r;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int rr = b * 16 + 4 * q + j;
+          const int rr = b * 16 + acc_row(spread, q, j);
           if (rr < tl.rows) h[static_cast<size_t>(tl.row0 + rr) * I + i] = f32_to_bf16(silu(G[j]) * U_[j]);
         }
       }
@@ -523,7 +547,7 @@ __global__ __launch_bounds__(256) void k_gateup_t(
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int rr = b * 16 + 4 * q + j;
+          const int rr = b * 16 + acc_row(spread, q, j);
           if (rr < tl.rows)
             h[static_cast<size_t>(tl.row0 + rr) * I + i] =
                 f32_to_bf16(silu(acc[mb][0][b][j]) * acc[mb][1][b][j]);
@@ -563,13 +587,17 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
     if constexpr (PAIRY) return static_cast<size_t>(min(max(sorted_pair[tl.row0 + rr], 0), P - 1));
     else return static_cast<size_t>(tl.row0 + rr);
   };
-  size_t orow[NB][4];   // direct stores: the rows this lane writes (16 b + 4 q + j)
+  // low-bit tiles of at most 4 rows with the rows in LDS take the 4-row
+  // layout (acc_row)
+  const bool spread = SH && kRollLowBit<WF, NB>() && tl.rows <= 4;
+  size_t orow[NB][4];   // direct stores: the rows this lane writes (16 b + acc_row)
   if constexpr (!kStageOut) {
     const int q4 = (threadIdx.x & 63) >> 4;
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) orow[b][j] = out_row(min(b * 16 + 4 * q4 + j, tl.rows - 1));
+      for (int j = 0; j < 4; ++j)
+        orow[b][j] = out_row(min(b * 16 + acc_row(spread, q4, j), tl.rows - 1));
   }
   const int hp = 2 * I + 16;   // SH: LDS row pitch in bytes (rows 16 bytes = 4 banks apart)
   // wave index as a uniform value (the slab base below must live in SGPRs)
@@ -677,47 +705,63 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
     // unit u+1 are issued into its registers as soon as unit u is done with
     // them (as in k_gateup_t), so every weight load has one unit of
     // multiplies to arrive in.  Per accumulator the additions run in the
-    // order of compute() (chunk order within a unit, units in order).
-    TScales sc[MB];
-    TRaw<WF> raw[MB];
-    auto load_blk = [&](int mb, int u) {
-      sc[mb] = tscales<WF, weight_aux<NB>()>(Sd, mb, u, r);
-      raw[mb] = tload<WF, weight_aux<NB>()>(Sd, mb, u, lane);
-    };
-    auto unit = [&](int u, auto roll_tag) {
-      constexpr bool ROLL = decltype(roll_tag)::value;
-      u32x4_t ha[4];
-      f32x4_t corr[4];
-#pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        ha[st] = *reinterpret_cast<const u32x4_t*>(hs + r * hp + (128 * u + 32 * st + 8 * q) * 2);
-        corr[st] = mfma_bf16(ha[st], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
+    // order of compute() (chunk order within a unit, units in order).  SP:
+    // the 4-row layout, one scale FMA per product instead of four.
+    auto rolled = [&](auto sp_tag) {
+      constexpr bool SP = decltype(sp_tag)::value;
+      const int hrow = SP ? (r >> 2) : r;   // LDS rows past the tile repeat its last row
+      TScales sc[MB];
+      TRaw<WF> raw[MB];
+      auto load_blk = [&](int mb, int u) {
+        sc[mb] = tscales<WF, weight_aux<NB>()>(Sd, mb, u, r);
+        raw[mb] = tload<WF, weight_aux<NB>()>(Sd, mb, u, lane);
+      };
+      auto unit = [&](int u, auto roll_tag) {
+        constexpr bool ROLL = decltype(roll_tag)::value;
+        u32x4_t ha[4];
+        f32x4_t corr[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-          const u32x4_t wv = tdecode<WF>(raw[mb], st, dq);
-          const float sv = sc[mb].f32(st);
-          const f32x4_t pp = mfma_bf16(ha[st], wv, corr[st]);
+          ha[st] =
+              *reinterpret_cast<const u32x4_t*>(hs + hrow * hp + (128 * u + 32 * st + 8 * q) * 2);
+          corr[st] = mfma_bf16(ha[st], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+        }
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[mb][0][j] = fmaf(sv, pp[j], acc[mb][0][j]);
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+          for (int st = 0; st < 4; ++st) {
+            const u32x4_t wv = tdecode<WF>(raw[mb], st, dq);
+            const float sv = sc[mb].f32(st);
+            const f32x4_t pp = mfma_bf16(ha[st], wv, corr[st]);
+            if constexpr (SP) {
+              acc[mb][0][0] = fmaf(sv, pp[0], acc[mb][0][0]);
+            } else {
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[mb][0][j] = fmaf(sv, pp[j], acc[mb][0][j]);
+            }
+          }
+          SCHED_FENCE();   // block by block: each waits for its own loads only
+          if constexpr (ROLL) {
+            load_blk(mb, u + 1);
+            SCHED_FENCE();
+          }
         }
-        if constexpr (ROLL) {
-          SCHED_FENCE();
-          load_blk(mb, u + 1);
-          SCHED_FENCE();
-        }
+      };
+      // the first unit's weights are in flight while the rows are staged;
+      // issued block by block, in the loop body's order
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        load_blk(mb, 0);
+        SCHED_FENCE();
       }
+      stage_h();
+      SCHED_FENCE();
+      const int nu = I / 128;
+      for (int u = 0; u + 1 < nu; ++u) unit(u, std::true_type{});
+      unit(nu - 1, std::false_type{});
     };
-    // the first unit's weights are in flight while the rows are staged
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) load_blk(mb, 0);
-    stage_h();
-    SCHED_FENCE();
-    const int nu = I / 128;
-    for (int u = 0; u + 1 < nu; ++u) unit(u, std::true_type{});
-    unit(nu - 1, std::false_type{});
+    if (spread) rolled(std::true_type{});
+    else rolled(std::false_type{});
   } else if constexpr (SH && !PF) {
     // the first unit's weights are in flight while the rows are staged
     Stage s0;
@@ -735,7 +779,7 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
                             [&](int row, int col, u32x4_t v) {
                               *reinterpret_cast<u32x4_t*>(y + out_row(row) * H + col) = v;
                             },
-                            sl * 64 * MB);
+                            sl * 64 * MB, spread);
   } else {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -744,7 +788,7 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
       for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int rr = b * 16 + 4 * q + j;
+          const int rr = b * 16 + acc_row(spread, q, j);
           if (rr < tl.rows) y[orow[b][j] * H + n] = f32_to_bf16(acc[mb][b][j]);
         }
     }

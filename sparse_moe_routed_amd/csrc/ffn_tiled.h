@@ -287,6 +287,56 @@ __device__ __forceinline__ TScales tscales(const Slab<WF>& S, int mb, int kb, in
       __builtin_amdgcn_raw_buffer_load_b64(S.s, r * 8, (mb * (S.K / 128) + kb) * 128, AUX)};
 }
 
+// Prescaled int2 decode (the rolled 16-row-tile kernels).  Dword m of a
+// chunk's B fragment holds stored codes 2m and 2m+1 (low and high bf16
+// half).  For m = 0, 1, 2 the code is masked where it lies in the byte of
+// its chunk (bits 2m of each half) instead of being shifted down, which
+// gives the exact bf16 value 128 + 4^m c (c = stored code); dword 3 is
+// shifted as before (128 + c).  Token dword m of the A fragment is divided
+// by 4^m beforehand (prescale_x_int2), so each product x 4^-m (128 + 4^m c)
+// = 128 x 4^-m + x c still carries the code once, and the correction
+// fragment (neg_offset_fragment_ps) holds -(128 + 4^m 2) per dword, making
+// the sum exactly x (c - 2) per term up to the MFMA's float32 rounding.
+// Five VALU per chunk of 8 codes instead of seven (sub-chunk 0), six
+// instead of eight (sub-chunk 1).
+struct DqPs {
+  uint32_t m0, m1, m2, magic;
+};
+__device__ __forceinline__ DqPs dq_ps_consts() {
+  return DqPs{in_vgpr(0x00030003u), in_vgpr(0x000C000Cu), in_vgpr(0x00300030u),
+              in_vgpr(0x43004300u)};
+}
+__device__ __forceinline__ u32x4_t tdecode_int2_ps(const TRaw<WF_INT2>& t, int s, DqPs d) {
+  const uint32_t w = t.v[0][s >> 1];
+  const uint32_t ws = (s & 1) ? (w >> 8) : w;
+  u32x4_t r;
+  r[0] = (ws & d.m0) | d.magic;
+  r[1] = (ws & d.m1) | d.magic;
+  r[2] = (ws & d.m2) | d.magic;
+  r[3] = ((w >> ((s & 1) ? 14 : 6)) & d.m0) | d.magic;
+  return r;
+}
+__device__ __forceinline__ u32x4_t neg_offset_fragment_ps() {
+  // bf16 pairs (-130), (-136), (-160), (-130)
+  return u32x4_t{kNegOffset2, 0xC308C308u, 0xC320C320u, kNegOffset2};
+}
+// Both bf16 halves of w divided by 2^(2 e) (e = 1 or 2): the exponent field
+// lowered by 2 e with a saturating 16-bit subtraction on the magnitude, the
+// sign kept.  Exact for |x| >= 2^-122; zeros stay zero, smaller magnitudes
+// flush towards zero.
+__device__ __forceinline__ uint32_t bf16x2_div_pow4(uint32_t w, uint16_t exp_step) {
+  typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+  const u16x2_t m = __builtin_bit_cast(u16x2_t, w & 0x7fff7fffu);
+  const u16x2_t r = __builtin_elementwise_sub_sat(m, u16x2_t{exp_step, exp_step});
+  return __builtin_bit_cast(uint32_t, r) | (w & 0x80008000u);
+}
+// A token fragment prepared for tdecode_int2_ps: dword 1 / 4, dword 2 / 16.
+__device__ __forceinline__ u32x4_t prescale_x_int2(u32x4_t v) {
+  v[1] = bf16x2_div_pow4(v[1], 0x0100);
+  v[2] = bf16x2_div_pow4(v[2], 0x0200);
+  return v;
+}
+
 template <int WF>
 __device__ __forceinline__ u32x4_t neg_offset_fragment() {
   const uint32_t c = (WF == WF_INT4) ? kNegOffset4 : kNegOffset2;

@@ -430,6 +430,10 @@ __global__ __launch_bounds__(256) void k_gateup_t(
     // second register stage.  Per accumulator the additions run in the same
     // order as in compute() (chunk order within a unit, units in order).
     // SP: the 4-row layout, one scale FMA per product instead of four.
+    // PS: int2 codes decoded in place against prescaled token fragments
+    // (tdecode_int2_ps)
+    constexpr bool PS = WF == WF_INT2;
+    const DqPs dps = dq_ps_consts();
     auto rolled = [&](auto sp_tag) {
       constexpr bool SP = decltype(sp_tag)::value;
       const uint16_t* pxr;
@@ -457,15 +461,23 @@ __global__ __launch_bounds__(256) void k_gateup_t(
         if constexpr (ROLL) load_x(xn, u + 1);
         f32x4_t corr[4];
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
-          corr[st] = mfma_bf16(xa[st], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+        for (int st = 0; st < 4; ++st) {
+          if constexpr (PS) {
+            xa[st] = prescale_x_int2(xa[st]);
+            corr[st] = mfma_bf16(xa[st], neg_offset_fragment_ps(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+          } else {
+            corr[st] = mfma_bf16(xa[st], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+          }
+        }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
           for (int gu = 0; gu < 2; ++gu) {
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-              const u32x4_t wv = tdecode<WF>(raw[mb][gu], st, dq);
+              u32x4_t wv;
+              if constexpr (PS) wv = tdecode_int2_ps(raw[mb][gu], st, dps);
+              else wv = tdecode<WF>(raw[mb][gu], st, dq);
               const float sv = sc[mb][gu].f32(st);
               const f32x4_t pp = mfma_bf16(xa[st], wv, corr[st]);
               if constexpr (SP) {
@@ -694,6 +706,9 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
         const int c = c0 + i * 256;
         if (c < nch) {
           const int row = c / cpr, c8 = c - row * cpr;
+          // int2 (rolled path): rows stored prescaled for tdecode_int2_ps
+          // (a 16-byte chunk is one MFMA A fragment of a lane)
+          if constexpr (WF == WF_INT2 && kRollLowBit<WF, NB>()) v[i] = prescale_x_int2(v[i]);
           *reinterpret_cast<u32x4_t*>(hs + row * hp + c8 * 16) = v[i];
         }
       }
@@ -707,6 +722,9 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
     // multiplies to arrive in.  Per accumulator the additions run in the
     // order of compute() (chunk order within a unit, units in order).  SP:
     // the 4-row layout, one scale FMA per product instead of four.
+    // PS: int2 codes decoded in place; the rows were prescaled when staged
+    constexpr bool PS = WF == WF_INT2;
+    const DqPs dps = dq_ps_consts();
     auto rolled = [&](auto sp_tag) {
       constexpr bool SP = decltype(sp_tag)::value;
       const int hrow = SP ? (r >> 2) : r;   // LDS rows past the tile repeat its last row
@@ -724,13 +742,18 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
         for (int st = 0; st < 4; ++st) {
           ha[st] =
               *reinterpret_cast<const u32x4_t*>(hs + hrow * hp + (128 * u + 32 * st + 8 * q) * 2);
-          corr[st] = mfma_bf16(ha[st], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+          if constexpr (PS)
+            corr[st] = mfma_bf16(ha[st], neg_offset_fragment_ps(), f32x4_t{0.f, 0.f, 0.f, 0.f});
+          else
+            corr[st] = mfma_bf16(ha[st], neg_offset_fragment<WF>(), f32x4_t{0.f, 0.f, 0.f, 0.f});
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
           for (int st = 0; st < 4; ++st) {
-            const u32x4_t wv = tdecode<WF>(raw[mb], st, dq);
+            u32x4_t wv;
+            if constexpr (PS) wv = tdecode_int2_ps(raw[mb], st, dps);
+            else wv = tdecode<WF>(raw[mb], st, dq);
             const float sv = sc[mb].f32(st);
             const f32x4_t pp = mfma_bf16(ha[st], wv, corr[st]);
             if constexpr (SP) {

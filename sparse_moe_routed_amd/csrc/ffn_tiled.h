@@ -323,7 +323,10 @@ __device__ __forceinline__ u32x4_t neg_offset_fragment_ps() {
 // Both bf16 halves of w divided by 2^(2 e) (e = 1 or 2): the exponent field
 // lowered by 2 e with a saturating 16-bit subtraction on the magnitude, the
 // sign kept.  Exact for |x| >= 2^-122; zeros stay zero, smaller magnitudes
-// flush towards zero.
+// flush towards zero.  An infinity or NaN becomes a finite value of
+// magnitude >= 2^124; its products with the decoded codes (>= 128) and with
+// the correction fragment overflow float32 with opposite signs, so a
+// non-finite token still makes the MFMA result NaN.
 __device__ __forceinline__ uint32_t bf16x2_div_pow4(uint32_t w, uint16_t exp_step) {
   typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
   const u16x2_t m = __builtin_bit_cast(u16x2_t, w & 0x7fff7fffu);

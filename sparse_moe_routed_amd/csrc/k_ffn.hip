@@ -326,6 +326,37 @@ constexpr bool kRollLowBit() {
   return WF != WF_BF16 && NB == 1;
 }
 
+// One row block's k unit in the rolled low-bit kernels: the four chunks are
+// decoded, then their four MFMAs issued back to back, then the group scales
+// applied, so each MFMA's latency is covered by the MFMAs after it (with the
+// chunks interleaved, every scale FMA waited for its MFMA with NOPs).  The
+// additions into `acc` run in chunk order.  PS: int2 codes decoded in place
+// (tdecode_int2_ps, token fragments prescaled); SP: the 4-row layout.
+template <int WF, bool PS, bool SP>
+__device__ __forceinline__ void rolled_block_unit(const TRaw<WF>& raw, const TScales& sc,
+                                                  const u32x4_t (&a)[4], const f32x4_t (&corr)[4],
+                                                  Dq dq, DqPs dps, f32x4_t& acc) {
+  u32x4_t wv[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    if constexpr (PS) wv[st] = tdecode_int2_ps(raw, st, dps);
+    else wv[st] = tdecode<WF>(raw, st, dq);
+  }
+  f32x4_t pp[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) pp[st] = mfma_bf16(a[st], wv[st], corr[st]);
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const float sv = sc.f32(st);
+    if constexpr (SP) {
+      acc[0] = fmaf(sv, pp[st][0], acc[0]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = fmaf(sv, pp[st][j], acc[j]);
+    }
+  }
+}
+
 template <int WF, int NB, int KSPLIT, int MB, bool PF>
 __global__ __launch_bounds__(256) void k_gateup_t(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ wg, const uint8_t* __restrict__ wu,
@@ -473,20 +504,8 @@ __global__ __launch_bounds__(256) void k_gateup_t(
         for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
           for (int gu = 0; gu < 2; ++gu) {
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-              u32x4_t wv;
-              if constexpr (PS) wv = tdecode_int2_ps(raw[mb][gu], st, dps);
-              else wv = tdecode<WF>(raw[mb][gu], st, dq);
-              const float sv = sc[mb][gu].f32(st);
-              const f32x4_t pp = mfma_bf16(xa[st], wv, corr[st]);
-              if constexpr (SP) {
-                acc[mb][gu][0][0] = fmaf(sv, pp[0], acc[mb][gu][0][0]);
-              } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[mb][gu][0][j] = fmaf(sv, pp[j], acc[mb][gu][0][j]);
-              }
-            }
+            rolled_block_unit<WF, PS, SP>(raw[mb][gu], sc[mb][gu], xa, corr, dq, dps,
+                                          acc[mb][gu][0]);
             SCHED_FENCE();   // pair by pair: each waits for its own loads only
             if constexpr (ROLL) {
               load_pair(mb, gu, u + 1);
@@ -749,20 +768,7 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-          for (int st = 0; st < 4; ++st) {
-            u32x4_t wv;
-            if constexpr (PS) wv = tdecode_int2_ps(raw[mb], st, dps);
-            else wv = tdecode<WF>(raw[mb], st, dq);
-            const float sv = sc[mb].f32(st);
-            const f32x4_t pp = mfma_bf16(ha[st], wv, corr[st]);
-            if constexpr (SP) {
-              acc[mb][0][0] = fmaf(sv, pp[0], acc[mb][0][0]);
-            } else {
-#pragma unroll
-              for (int j = 0; j < 4; ++j) acc[mb][0][j] = fmaf(sv, pp[j], acc[mb][0][j]);
-            }
-          }
+          rolled_block_unit<WF, PS, SP>(raw[mb], sc[mb], ha, corr, dq, dps, acc[mb][0]);
           SCHED_FENCE();   // block by block: each waits for its own loads only
           if constexpr (ROLL) {
             load_blk(mb, u + 1);

@@ -708,8 +708,9 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
     }
   };
   auto stage_h = [&]() {
-    // 16-byte chunks; rows past the tile repeat its last row (never stored)
-    const int cpr = I / 8, nch = 16 * NB * cpr;
+    // 16-byte chunks; rows past the tile repeat its last row (never stored).
+    // The 4-row layout reads rows 0 .. 3 only.
+    const int cpr = I / 8, nch = (spread ? 4 : 16 * NB) * cpr;
     for (int c0 = threadIdx.x; c0 < nch; c0 += 4 * 256) {
       u32x4_t v[4];
 #pragma unroll

@@ -364,7 +364,10 @@ __global__ __launch_bounds__(256) void k_gateup_t(
     const int32_t* __restrict__ tiles, int max_tiles, const int32_t* __restrict__ sorted_pair,
     int k, int H, int I, int P, uint16_t* __restrict__ h, int band, int xcd) {
   constexpr int RG = 4 / KSPLIT;
-  constexpr int RB = MB < 2 ? MB : 2;              // row blocks reduced per LDS pass
+  // row blocks reduced per LDS pass: all of them for the low-bit 16-row
+  // tiles (one barrier round, 32 KB at MB = 4; verify_int2 gate/up 21.8 ->
+  // 21.2 us), two otherwise
+  constexpr int RB = kRollLowBit<WF, NB>() ? MB : (MB < 2 ? MB : 2);
   __shared__ f32x4_t red[KSPLIT > 1 ? 4 : 1][RB][2][NB][64];
   int ti, sl;
   if (!tile_item(tiles[3 * max_tiles], I / (16 * MB * RG), band, xcd != 0, ti, sl)) return;

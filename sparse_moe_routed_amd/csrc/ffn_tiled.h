@@ -124,10 +124,9 @@ constexpr int out_tile_bytes() {
 }
 // With a store functor: store(row, col, v) writes the 16 bytes v of tile row
 // `row` at column `col` (8 values) wherever the caller keeps them.
-// `spread`: the accumulators are in the 4-row layout (acc_row).
 template <int NB, int MB, typename Val, typename Store>
 __device__ __forceinline__ void store_tile_rows(char* lds, Val&& val, int rows, Store store,
-                                                int col0, bool spread = false) {
+                                                int col0) {
   constexpr int pitch = 128 * MB + 16;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, q = lane >> 4;
@@ -138,7 +137,7 @@ __device__ __forceinline__ void store_tile_rows(char* lds, Val&& val, int rows, 
     for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint16_t*>(lds + (16 * b + acc_row(spread, q, j)) * pitch +
+        *reinterpret_cast<uint16_t*>(lds + (16 * b + 4 * q + j) * pitch +
                                      (16 * (MB * wave + mb) + r) * 2) = f32_to_bf16(val(mb, b, j));
   __syncthreads();
   constexpr int segs = 8 * MB;          // 16-byte segments per row

@@ -625,6 +625,9 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
   // layout (acc_row)
   const bool spread = SH && kRollLowBit<WF, NB>() && tl.rows <= 4;
   size_t orow[NB][4];   // direct stores: the rows this lane writes (16 b + acc_row)
+  // 4-row layout: the output row of lane quarter q (its component 0), read
+  // now so that the direct stores at the end do not wait for it
+  const size_t srow = spread ? out_row(min((static_cast<int>(threadIdx.x) & 63) >> 4, tl.rows - 1)) : 0;
   if constexpr (!kStageOut) {
     const int q4 = (threadIdx.x & 63) >> 4;
 #pragma unroll
@@ -808,11 +811,20 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
     unit_loop<PF, Stage>(0, I / 128, load, compute);
   }
   if constexpr (kStageOut) {
-    store_tile_rows<NB, MB>(ot, [&](int mb, int b, int j) { return acc[mb][b][j]; }, tl.rows,
-                            [&](int row, int col, u32x4_t v) {
-                              *reinterpret_cast<u32x4_t*>(y + out_row(row) * H + col) = v;
-                            },
-                            sl * 64 * MB, spread);
+    if (spread) {
+      // at most 4 rows: direct 2-byte stores of component 0 (row q), no
+      // round trip through LDS and its two barriers
+      if (q < tl.rows) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) y[srow * H + n0 + mb * 16 + r] = f32_to_bf16(acc[mb][0][0]);
+      }
+    } else {
+      store_tile_rows<NB, MB>(ot, [&](int mb, int b, int j) { return acc[mb][b][j]; }, tl.rows,
+                              [&](int row, int col, u32x4_t v) {
+                                *reinterpret_cast<u32x4_t*>(y + out_row(row) * H + col) = v;
+                              },
+                              sl * 64 * MB);
+    }
   } else {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {

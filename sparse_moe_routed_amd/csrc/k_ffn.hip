@@ -716,11 +716,14 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
   auto stage_h = [&]() {
     // 16-byte chunks; rows past the tile repeat its last row (never stored).
     // The 4-row layout reads rows 0 .. 3 only.
+    // Up to 8 chunks per thread in flight: one round of loads for 16 rows at
+    // I <= 1024.
+    constexpr int SB = 8;
     const int cpr = I / 8, nch = (spread ? 4 : 16 * NB) * cpr;
-    for (int c0 = threadIdx.x; c0 < nch; c0 += 4 * 256) {
-      u32x4_t v[4];
+    for (int c0 = threadIdx.x; c0 < nch; c0 += SB * 256) {
+      u32x4_t v[SB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < SB; ++i) {
         const int c = c0 + i * 256;
         if (c < nch) {
           const int row = c / cpr, c8 = c - row * cpr;
@@ -728,7 +731,7 @@ __global__ __launch_bounds__(256) void k_down_t(const uint16_t* __restrict__ h,
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < SB; ++i) {
         const int c = c0 + i * 256;
         if (c < nch) {
           const int row = c / cpr, c8 = c - row * cpr;

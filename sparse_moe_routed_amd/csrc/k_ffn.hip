@@ -454,7 +454,7 @@ __global__ __launch_bounds__(256) void k_gateup_t(
       }
     }
   };
-  // low-bit tiles of at most 4 rows take the 4-row layout (spread_rows)
+  // low-bit tiles of at most 4 rows take the 4-row layout (acc_row)
   const bool spread = kRollLowBit<WF, NB>() && tl.rows <= 4;
   if constexpr (kRollLowBit<WF, NB>()) {
     // low-bit, one token block: the loads of a (row block, gate/up) pair

@@ -1,12 +1,13 @@
-"""The int2 16-row-tile FFN kernels on token values chosen for their in-place
-code decode.  Token dwords 1 and 2 of every MFMA fragment are divided by 4
-and 16 with an exponent step before they meet codes masked in place, and
-the SwiGLU rows feeding down are staged that way too.  So zero and
-negative-zero elements, all-zero rows, small magnitudes and mixed signs must
-come out of gate/up and down as the float64 oracle computes them, in tiles
-of both layouts (at most 4 rows, and more).  A non-finite token value, in a
-prescaled dword or not, must make every output of that token non-finite and
-leave the other tokens' outputs as they are.
+"""The low-bit 16-row-tile FFN kernels on chosen token values.  For int2,
+token dwords 1 and 2 of every MFMA fragment are divided by 4 and 16 with an
+exponent step before they meet codes masked in place, and the SwiGLU rows
+feeding down are staged that way too; for both formats tiles of at most 4
+rows use the 4-row layout.  So zero and negative-zero elements, all-zero
+rows, small magnitudes and mixed signs must come out of gate/up and down as
+the float64 oracle computes them, in tiles of both layouts (at most 4 rows,
+and more).  A non-finite token value, in a prescaled dword or not, must make
+every output of that token non-finite and leave the other tokens' outputs as
+they are.
 
 Expected values: the oracle's SwiGLU intermediate and down projection on the
 same expert records ("Agent Field Notes -- full corpus", AFN-001, section
@@ -23,9 +24,11 @@ from tests.gpu_util import DEV, buffers, check_values, decode, i32, make_case, s
 
 pytestmark = pytest.mark.gpu
 
-# int2 g32 experts, tiled; H = 1024: four k parts of two 128-wide units per
-# gate/up wave (a rolled unit and the last one), I = 256: two units in down
+# low-bit g32 experts, tiled; H = 1024: four k parts of two 128-wide units
+# per gate/up wave (a rolled unit and the last one), I = 256: two units in
+# down
 CFG = CONFIGS[5].with_(T=24, H=1024, E=32, I=256, k=4, layers=1)
+WFMTS = ["int2_g32", "int4_g32"]
 TINY = 2.0 ** -40
 
 
@@ -69,9 +72,10 @@ def rel_check(got, ref, what):
     return err
 
 
+@pytest.mark.parametrize("wfmt", WFMTS)
 @pytest.mark.parametrize("poisoned", [False, True], ids=["finite", "nonfinite"])
-def test_int2_gateup_special_tokens(poisoned):
-    cfg = CFG
+def test_lowbit_gateup_special_tokens(poisoned, wfmt):
+    cfg = CFG.with_(wfmt=wfmt)
     case = make_case(cfg)
     rng = np.random.default_rng(5)
     ids = forced_ids(cfg.T)
@@ -81,13 +85,13 @@ def test_int2_gateup_special_tokens(poisoned):
     if poisoned:
         x64 = poison(x64, bad)
     buf = buffers(cfg, tiled=True)
-    say(f"[int2 prescale gate/up poisoned={poisoned}] moe_permute on forced ids")
+    say(f"[{wfmt} special values gate/up poisoned={poisoned}] moe_permute on forced ids")
     buf.permute(topk_ids=i32(ids))
     torch.cuda.synchronize()
     assert np.array_equal(buf.sorted_pair.cpu().numpy(), ref_perm.sorted_pair)
     rows_per_expert = np.diff(ref_perm.offsets)[ref_perm.active]
     assert (rows_per_expert <= 4).any() and (rows_per_expert > 4).any()
-    say(f"[int2 prescale gate/up poisoned={poisoned}] moe_ffn_gate_up")
+    say(f"[{wfmt} special values gate/up poisoned={poisoned}] moe_ffn_gate_up")
     buf.ffn_gate_up(to_act_tensor(x64, "bf16"), case.experts(True))
     torch.cuda.synchronize()
     got = decode(buf.h, "bf16")
@@ -102,12 +106,13 @@ def test_int2_gateup_special_tokens(poisoned):
     rel = rel_check(got[small], A[small], "h (small token)")
     zero = tok == 0
     assert (got[zero] == 0).all(), "an all-zero token gave nonzero outputs"
-    say(f"[int2 prescale gate/up poisoned={poisoned}] h {stats}, small-token rel {rel:.3g}")
+    say(f"[{wfmt} special values gate/up poisoned={poisoned}] h {stats}, small-token rel {rel:.3g}")
 
 
+@pytest.mark.parametrize("wfmt", WFMTS)
 @pytest.mark.parametrize("poisoned", [False, True], ids=["finite", "nonfinite"])
-def test_int2_down_special_rows(poisoned):
-    cfg = CFG
+def test_lowbit_down_special_rows(poisoned, wfmt):
+    cfg = CFG.with_(wfmt=wfmt)
     case = make_case(cfg)
     rng = np.random.default_rng(6)
     ids = forced_ids(cfg.T)
@@ -129,7 +134,7 @@ def test_int2_down_special_rows(poisoned):
             c, v = kinds[i % 3]
             A[r, c] = v
     buf = buffers(cfg, tiled=True)
-    say(f"[int2 prescale down poisoned={poisoned}] moe_permute + moe_ffn_down")
+    say(f"[{wfmt} special values down poisoned={poisoned}] moe_permute + moe_ffn_down")
     buf.permute(topk_ids=i32(ids))
     buf.ffn_down(case.experts(True), h=to_act_tensor(A, "bf16"))
     torch.cuda.synchronize()
@@ -145,4 +150,4 @@ def test_int2_down_special_rows(poisoned):
     rel = rel_check(got[small], Y[small], "y (small rows)")
     zero = tok == 0
     assert (got[zero] == 0).all(), "all-zero rows gave nonzero outputs"
-    say(f"[int2 prescale down poisoned={poisoned}] y {stats}, small-row rel {rel:.3g}")
+    say(f"[{wfmt} special values down poisoned={poisoned}] y {stats}, small-row rel {rel:.3g}")

@@ -275,6 +275,87 @@ __global__ __launch_bounds__(1024) void k_perm_place(const int32_t* __restrict__
   }
 }
 
+// Scan and placement in one launch for up to kScanPlaceChunks chunks: every
+// workgroup adds the chunk counts of all chunks itself (E x C loads, one
+// round) instead of reading the bases a single-workgroup scan kernel wrote,
+// and workgroup 0 also publishes the counts, offsets, active list and tile
+// plan.  Same rows as k_perm_scan + k_perm_place (integer sums, chunk and
+// token order); one launch fewer.
+constexpr int kScanPlaceChunks = 16;
+__global__ __launch_bounds__(1024) void k_perm_scan_place(
+    const int32_t* __restrict__ ids, int T, int k, int E, const int32_t* __restrict__ chunk_cnt,
+    int nchunks, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ active, int32_t* __restrict__ n_active, int rt, int max_tiles,
+    int32_t* __restrict__ tiles, int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_row) {
+  __shared__ int s_cnt[1024];
+  __shared__ int s_off[1024];
+  __shared__ int s_base[1024];
+  __shared__ int s_act[1024];
+  __shared__ int s_tot[17];
+  __shared__ uint32_t bits[1024 * kChunkWords];
+  const int tid = threadIdx.x, c = blockIdx.x;
+  const int P = T * k;
+  int run = 0;
+  if (tid < E) {
+    int v[kScanPlaceChunks];
+#pragma unroll
+    for (int u = 0; u < kScanPlaceChunks; ++u)
+      v[u] = u < nchunks ? chunk_cnt[static_cast<size_t>(u) * E + tid] : 0;
+    int base = 0;
+#pragma unroll
+    for (int u = 0; u < kScanPlaceChunks; ++u) {
+      if (u == c) base = run;
+      run += v[u];
+    }
+    s_cnt[tid] = run;
+    s_base[tid] = base;
+  }
+  int total = 0;
+  const int ex = block_excl_scan(tid < E ? run : 0, s_tot, &total);
+  if (tid < E) s_off[tid] = ex;
+  if (c == 0) {
+    if (tid < E) {
+      counts[tid] = run;
+      offsets[tid] = ex;
+      if (tid == E - 1) offsets[E] = ex + run;
+    }
+    const int flag = (tid < E && run > 0) ? 1 : 0;
+    int nact = 0;
+    const int apos = block_excl_scan(flag, s_tot, &nact);
+    if (flag) {
+      active[apos] = tid;
+      s_act[apos] = tid;
+    }
+    if (tid < E && tid >= nact) active[tid] = -1;
+    if (tid == 0) n_active[0] = nact;
+    __syncthreads();
+    if (tiles != nullptr) emit_tiles(nact, s_act, s_cnt, s_off, P, rt, max_tiles, tiles, s_tot);
+  }
+  // placement of this chunk's pairs (as k_perm_place)
+  const int t0 = c * kChunkTok;
+  for (int i = tid; i < E * kChunkWords; i += blockDim.x) bits[i] = 0u;
+  __syncthreads();
+  const int p0 = t0 * k, p1 = min(T, t0 + kChunkTok) * k;
+  for (int p = p0 + tid; p < p1; p += blockDim.x) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) {
+      const int t = p / k - t0;
+      atomicOr(&bits[e * kChunkWords + (t >> 5)], 1u << (t & 31));
+    }
+  }
+  __syncthreads();
+  for (int p = p0 + tid; p < p1; p += blockDim.x) {
+    const int e = ids[p];
+    if (e < 0 || e >= E) continue;
+    const int t = p / k - t0;
+    const int wi = t >> 5;
+    int row = s_off[e] + s_base[e] + __popc(bits[e * kChunkWords + wi] & ((1u << (t & 31)) - 1u));
+    for (int w = 0; w < wi; ++w) row += __popc(bits[e * kChunkWords + w]);
+    sorted_pair[row] = p;
+    pair_row[p] = row;
+  }
+}
+
 // Tile plan from an existing permutation (for moe_grouped_ffn, whose caller
 // may supply any permutation).  Values are clamped so that tiles never
 // address rows outside [0, P).
@@ -321,12 +402,17 @@ hipError_t launch_permute(const moe_shape& s, const Plan& pl, const int32_t* ids
     int32_t* chunk_cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + pl.chunk_off);
     int32_t* chunk_base = chunk_cnt + static_cast<size_t>(C) * s.E;
     hipLaunchKernelGGL(k_perm_count, dim3(C), dim3(1024), 0, st, ids, s.T, s.top_k, s.E, chunk_cnt);
-    hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, st, chunk_cnt, C, s.T, s.top_k, s.E,
-                       chunk_base, pp.counts, pp.offsets, pp.active, pp.n_active, rt, pl.max_tiles,
-                       tiles);
-    hipLaunchKernelGGL(k_perm_place, dim3(C), dim3(1024), 0, st, ids, s.T, s.top_k, s.E, chunk_base,
-                       pp.offsets,
-                       pp.sorted_pair, pp.pair_row);
+    if (C <= kScanPlaceChunks) {
+      hipLaunchKernelGGL(k_perm_scan_place, dim3(C), dim3(1024), 0, st, ids, s.T, s.top_k, s.E,
+                         chunk_cnt, C, pp.counts, pp.offsets, pp.active, pp.n_active, rt,
+                         pl.max_tiles, tiles, pp.sorted_pair, pp.pair_row);
+    } else {
+      hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, st, chunk_cnt, C, s.T, s.top_k, s.E,
+                         chunk_base, pp.counts, pp.offsets, pp.active, pp.n_active, rt,
+                         pl.max_tiles, tiles);
+      hipLaunchKernelGGL(k_perm_place, dim3(C), dim3(1024), 0, st, ids, s.T, s.top_k, s.E,
+                         chunk_base, pp.offsets, pp.sorted_pair, pp.pair_row);
+    }
   }
   return hipGetLastError();
 }

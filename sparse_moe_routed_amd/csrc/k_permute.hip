@@ -275,13 +275,20 @@ __global__ __launch_bounds__(1024) void k_perm_place(const int32_t* __restrict__
   }
 }
 
-// Scan and placement in one launch for up to kScanPlaceChunks chunks: every
-// workgroup adds the chunk counts of all chunks itself (E x C loads, one
-// round) instead of reading the bases a single-workgroup scan kernel wrote,
-// and workgroup 0 also publishes the counts, offsets, active list and tile
-// plan.  Same rows as k_perm_scan + k_perm_place (integer sums, chunk and
-// token order); one launch fewer.
+// Scan and placement in one launch for up to kScanPlaceChunks chunks (4096
+// tokens): every workgroup forms the expert counts of all pairs, and of the
+// pairs of the chunks before its own, itself, instead of reading bases that
+// a single-workgroup scan launch wrote; workgroup 0 also publishes the
+// counts, offsets, active list and tile plan.  COUNT (up to kCountChunks
+// chunks): the counts come from a histogram of all pairs' ids in LDS, so
+// the count launch goes too; otherwise from k_perm_count's per-chunk counts
+// (one round of E x C loads).  Same rows as k_perm_count + k_perm_scan +
+// k_perm_place (integer sums, chunk and token order).  Measured: 512
+// tokens (2 chunks) step -1.3% with COUNT; 4096 tokens (16 chunks) -0.3%
+// without it and +0.8% with it.
 constexpr int kScanPlaceChunks = 16;
+constexpr int kCountChunks = 4;
+template <bool COUNT>
 __global__ __launch_bounds__(1024) void k_perm_scan_place(
     const int32_t* __restrict__ ids, int T, int k, int E, const int32_t* __restrict__ chunk_cnt,
     int nchunks, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -295,13 +302,28 @@ __global__ __launch_bounds__(1024) void k_perm_scan_place(
   __shared__ uint32_t bits[1024 * kChunkWords];
   const int tid = threadIdx.x, c = blockIdx.x;
   const int P = T * k;
-  int run = 0;
-  if (tid < E) {
+  const int t0 = c * kChunkTok;
+  const int p0 = t0 * k, p1 = min(T, t0 + kChunkTok) * k;
+  for (int i = tid; i < E * kChunkWords; i += blockDim.x) bits[i] = 0u;
+  if constexpr (COUNT) {
+    for (int e = tid; e < E; e += blockDim.x) {
+      s_cnt[e] = 0;
+      s_base[e] = 0;
+    }
+    __syncthreads();
+    for (int p = tid; p < P; p += blockDim.x) {
+      const int e = ids[p];
+      if (e >= 0 && e < E) {
+        atomicAdd(&s_cnt[e], 1);
+        if (p < p0) atomicAdd(&s_base[e], 1);
+      }
+    }
+  } else if (tid < E) {
     int v[kScanPlaceChunks];
 #pragma unroll
     for (int u = 0; u < kScanPlaceChunks; ++u)
       v[u] = u < nchunks ? chunk_cnt[static_cast<size_t>(u) * E + tid] : 0;
-    int base = 0;
+    int run = 0, base = 0;
 #pragma unroll
     for (int u = 0; u < kScanPlaceChunks; ++u) {
       if (u == c) base = run;
@@ -310,8 +332,10 @@ __global__ __launch_bounds__(1024) void k_perm_scan_place(
     s_cnt[tid] = run;
     s_base[tid] = base;
   }
+  __syncthreads();
+  const int run = tid < E ? s_cnt[tid] : 0;
   int total = 0;
-  const int ex = block_excl_scan(tid < E ? run : 0, s_tot, &total);
+  const int ex = block_excl_scan(run, s_tot, &total);
   if (tid < E) s_off[tid] = ex;
   if (c == 0) {
     if (tid < E) {
@@ -332,10 +356,6 @@ __global__ __launch_bounds__(1024) void k_perm_scan_place(
     if (tiles != nullptr) emit_tiles(nact, s_act, s_cnt, s_off, P, rt, max_tiles, tiles, s_tot);
   }
   // placement of this chunk's pairs (as k_perm_place)
-  const int t0 = c * kChunkTok;
-  for (int i = tid; i < E * kChunkWords; i += blockDim.x) bits[i] = 0u;
-  __syncthreads();
-  const int p0 = t0 * k, p1 = min(T, t0 + kChunkTok) * k;
   for (int p = p0 + tid; p < p1; p += blockDim.x) {
     const int e = ids[p];
     if (e >= 0 && e < E) {
@@ -401,12 +421,19 @@ hipError_t launch_permute(const moe_shape& s, const Plan& pl, const int32_t* ids
     const int C = permute_chunks(s);
     int32_t* chunk_cnt = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + pl.chunk_off);
     int32_t* chunk_base = chunk_cnt + static_cast<size_t>(C) * s.E;
-    hipLaunchKernelGGL(k_perm_count, dim3(C), dim3(1024), 0, st, ids, s.T, s.top_k, s.E, chunk_cnt);
-    if (C <= kScanPlaceChunks) {
-      hipLaunchKernelGGL(k_perm_scan_place, dim3(C), dim3(1024), 0, st, ids, s.T, s.top_k, s.E,
-                         chunk_cnt, C, pp.counts, pp.offsets, pp.active, pp.n_active, rt,
+    if (C <= kCountChunks) {
+      hipLaunchKernelGGL(k_perm_scan_place<true>, dim3(C), dim3(1024), 0, st, ids, s.T, s.top_k,
+                         s.E, nullptr, C, pp.counts, pp.offsets, pp.active, pp.n_active, rt,
+                         pl.max_tiles, tiles, pp.sorted_pair, pp.pair_row);
+    } else if (C <= kScanPlaceChunks) {
+      hipLaunchKernelGGL(k_perm_count, dim3(C), dim3(1024), 0, st, ids, s.T, s.top_k, s.E,
+                         chunk_cnt);
+      hipLaunchKernelGGL(k_perm_scan_place<false>, dim3(C), dim3(1024), 0, st, ids, s.T, s.top_k,
+                         s.E, chunk_cnt, C, pp.counts, pp.offsets, pp.active, pp.n_active, rt,
                          pl.max_tiles, tiles, pp.sorted_pair, pp.pair_row);
     } else {
+      hipLaunchKernelGGL(k_perm_count, dim3(C), dim3(1024), 0, st, ids, s.T, s.top_k, s.E,
+                         chunk_cnt);
       hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, st, chunk_cnt, C, s.T, s.top_k, s.E,
                          chunk_base, pp.counts, pp.offsets, pp.active, pp.n_active, rt,
                          pl.max_tiles, tiles);

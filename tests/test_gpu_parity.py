@@ -112,9 +112,12 @@ def test_permute(name):
 
 # Seeded random routes (distinct experts per token) across the permutation
 # paths: 32-token kernel, one workgroup (bitmap + prefixes up to 48 KB of
-# LDS), chunked (beyond it); the boundary shapes on both sides of each.
+# LDS), chunked beyond it (256-token chunks: one launch up to 4 chunks, count
+# + merged scan and placement up to 16, three launches beyond); the boundary
+# shapes on both sides of each.
 PERM_RANDOM = [(1, 10, 512), (32, 10, 512), (33, 10, 512), (384, 10, 512), (385, 10, 512),
-               (1025, 10, 512), (2000, 10, 512), (192, 8, 1024), (193, 8, 1024), (700, 1, 16)]
+               (1024, 10, 512), (1025, 10, 512), (2000, 10, 512), (4096, 10, 512),
+               (4097, 10, 512), (192, 8, 1024), (193, 8, 1024), (700, 1, 16)]
 
 
 @pytest.mark.parametrize("T,k,E", PERM_RANDOM)
